@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random tensors and describes workload shapes; it
+holds none of the attention arithmetic.  Both the GPU tests/benchmark and
+the CPU oracle are fed from it.
+
+Recipe: a torch CPU generator seeded with `seed` draws, in order,
+(group mode only) the sequence lengths with randint(lo, hi+1), then
+Q, K, V, [bias], dO as float32 standard normals, each then rounded to the io
+dtype (round to nearest even).  Tensors are dense BHSD (batch mode) or packed
+THD with cu_seqlens = [0, cumsum(lengths)] (group mode).
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+DROPOUT_SEED = 0x9E3779B97F4A7C15
+
+_IO = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    b: int
+    h: int
+    s_q: int
+    s_kv: int
+    d_qk: int
+    d_v: int
+    causal: bool = False
+    bias: bool = False
+    dropout_p: float = 0.0
+    seed: int = 0
+    # group (varlen) mode: number of sequences and the length range
+    varlen: Optional[tuple] = None  # (n_seq, lo, hi)
+    scale: Optional[float] = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else self.d_qk ** -0.5
+
+
+# The five workloads of the benchmark suite (seed 1000 + index).
+WORKLOADS = {
+    1: Workload("fp32 B1 H2 S128 d64", "f32", 1, 2, 128, 128, 64, 64, seed=1001),
+    2: Workload("bf16 causal B4 H16 S2048 d128", "bf16", 4, 16, 2048, 2048, 128, 128,
+                causal=True, seed=1002),
+    3: Workload("fp16 bias B2 H32 Sq1024 Skv4096 dqk192 dv128", "f16", 2, 32, 1024, 4096,
+                192, 128, bias=True, seed=1003),
+    4: Workload("bf16 varlen 16 seqs L~U[64,4096] H16 d128 causal", "bf16", 16, 16, 4096, 4096,
+                128, 128, causal=True, varlen=(16, 64, 4096), seed=1004),
+    5: Workload("bf16 causal dropout0.1 B2 H16 S4096 d128", "bf16", 2, 16, 4096, 4096, 128, 128,
+                causal=True, dropout_p=0.1, seed=1005),
+}
+
+
+def make_inputs(wl: Workload, lengths=None):
+    """Draw the workload's tensors on the CPU.  Returns a dict with
+    q, k, v, dout, [bias], [lengths, cu_seqlens] and the io dtype."""
+    g = torch.Generator().manual_seed(wl.seed)
+    io = _IO[wl.dtype]
+    out = {"dtype": io}
+    if wl.varlen is not None:
+        n, lo, hi = wl.varlen
+        if lengths is None:
+            lengths = torch.randint(lo, hi + 1, (n,), generator=g)
+        else:
+            lengths = torch.as_tensor(lengths, dtype=torch.int64)
+        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
+        T = int(cu[-1])
+        shp_q, shp_k, shp_v, shp_o = (T, wl.h, wl.d_qk), (T, wl.h, wl.d_qk), (T, wl.h, wl.d_v), (T, wl.h, wl.d_v)
+        out["lengths"] = lengths
+        out["cu_seqlens"] = cu
+        out["max_seqlen"] = int(lengths.max()) if len(lengths) else 0
+    else:
+        shp_q = (wl.b, wl.h, wl.s_q, wl.d_qk)
+        shp_k = (wl.b, wl.h, wl.s_kv, wl.d_qk)
+        shp_v = (wl.b, wl.h, wl.s_kv, wl.d_v)
+        shp_o = (wl.b, wl.h, wl.s_q, wl.d_v)
+    out["q"] = torch.randn(shp_q, generator=g, dtype=torch.float32).to(io)
+    out["k"] = torch.randn(shp_k, generator=g, dtype=torch.float32).to(io)
+    out["v"] = torch.randn(shp_v, generator=g, dtype=torch.float32).to(io)
+    if wl.bias:
+        out["bias"] = torch.randn((wl.b, wl.h, wl.s_q, wl.s_kv), generator=g,
+                                  dtype=torch.float32).to(io)
+    out["dout"] = torch.randn(shp_o, generator=g, dtype=torch.float32).to(io)
+    return out
+
+
+def small(dtype="bf16", b=1, h=2, s_q=200, s_kv=200, d_qk=128, d_v=128, causal=False,
+          bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None) -> Workload:
+    """A small workload (parity-test size) with the same recipe."""
+    return Workload(f"small-{dtype}", dtype, b, h, s_q, s_kv, d_qk, d_v, causal=causal, bias=bias,
+                    dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale)

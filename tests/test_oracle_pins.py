@@ -1,0 +1,372 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle.
+
+Every test here runs on the CPU.  What pins what:
+  - Philox4x32-10: published known-answer vectors, and rocRAND's engine run
+    on the host.
+  - keep mask: drop-rate statistics, seed/offset sensitivity, p = 0 identity.
+  - forward: closed forms (S_kv = 1, Q = 0, causal prefix means), key
+    permutation invariance, and torch's float64 scaled_dot_product_attention
+    library routine; LSE against torch.logsumexp.
+  - backward: central finite differences of L = sum(dO o O) through the
+    oracle's own forward, torch float64 autograd of the forward, and
+    invariants (row sums of dS vanish, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+  - group mode: equals batch mode run sequence by sequence.
+  - mutation check: deliberately broken builds of the oracle fail the pins.
+"""
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.sdpa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- Philox ----
+def _kat():
+    rows = []
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            v = [int(x, 16) for x in line.split()]
+            rows.append((v[0:4], v[4:6], v[6:10]))
+    return rows
+
+
+def test_philox_known_answers():
+    rows = _kat()
+    assert len(rows) == 3
+    for ctr, key, want in rows:
+        assert O.philox4x32_10(ctr, key) == want
+
+
+def test_philox_matches_rocrand_engine(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = tmp_path / "rpc"
+    r = subprocess.run([hipcc, "-O1", os.path.join(ROOT, "tests", "rocrand_philox_check.cpp"),
+                        "-o", str(exe)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("rocRAND header not usable: " + r.stderr[-300:])
+    rng = np.random.default_rng(5)
+    cases = []
+    for _ in range(64):
+        c = [int(rng.integers(0, 2**32)), int(rng.integers(0, 2**30)),
+             int(rng.integers(0, 2**32)), int(rng.integers(0, 2**32))]
+        k = [int(rng.integers(0, 2**32)), int(rng.integers(0, 2**32))]
+        cases.append((c, k))
+    inp = "".join("%x %x %x %x %x %x\n" % (*c, *k) for c, k in cases)
+    out = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True).stdout
+    got = [[int(x, 16) for x in line.split()] for line in out.strip().splitlines()]
+    for (c, k), g in zip(cases, got):
+        assert O.philox4x32_10(c, k) == g
+
+
+def test_drop_threshold_values():
+    assert O.drop_threshold(0.0) == 0
+    assert O.drop_threshold(0.1) == 26       # round(25.6)
+    assert O.drop_threshold(0.5) == 128
+    assert O.drop_threshold(0.999) == 255
+
+
+def test_keep_mask_statistics_and_sensitivity():
+    B, H, S = 1, 2, 256
+    q = _rand((B, H, S, 16), 1)
+    k = _rand((B, H, S, 16), 2)
+    v = _rand((B, H, S, 16), 3)
+    seed = 0x9E3779B97F4A7C15
+    r0 = O.fwd(q, k, v, scale=0.25, p_drop=0.1, seed=seed, offset=0, want_keep=True)["keep"]
+    n = r0.size
+    rate = 1.0 - r0.mean()
+    p = 26 / 256
+    assert abs(rate - p) < 6 * math.sqrt(p * (1 - p) / n)
+    r1 = O.fwd(q, k, v, scale=0.25, p_drop=0.1, seed=seed, offset=1, want_keep=True)["keep"]
+    r2 = O.fwd(q, k, v, scale=0.25, p_drop=0.1, seed=seed + 1, offset=0, want_keep=True)["keep"]
+    # independent masks disagree on about 2 p (1 - p) of the elements
+    for other in (r1, r2):
+        frac = (other != r0).mean()
+        assert abs(frac - 2 * p * (1 - p)) < 0.02
+    # the two heads use different counters
+    assert (r0[0, 0] != r0[0, 1]).mean() > 0.1
+
+
+def test_dropout_zero_is_identity():
+    q, k, v = _rand((1, 2, 37, 8), 4), _rand((1, 2, 41, 8), 5), _rand((1, 2, 41, 6), 6)
+    a = O.fwd(q, k, v, scale=0.3, p_drop=0.0)
+    b = O.fwd(q, k, v, scale=0.3)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+
+
+# ------------------------------------------------------- forward pins -------
+def test_single_key_gives_v():
+    q, k, v = _rand((2, 3, 9, 5), 7), _rand((2, 3, 1, 5), 8), _rand((2, 3, 1, 4), 9)
+    bias = _rand((2, 3, 9, 1), 10)
+    r = O.fwd(q, k, v, scale=0.7, bias=bias)
+    assert np.allclose(r["o"], np.broadcast_to(v, r["o"].shape), atol=1e-12, rtol=0)
+    s00 = 0.7 * np.einsum("bhid,bhjd->bhij", q, k)[..., 0] + bias[..., 0]
+    assert np.allclose(r["lse"], s00, atol=1e-12, rtol=0)
+
+
+def test_zero_query_gives_mean_of_values():
+    q = np.zeros((1, 2, 7, 5))
+    k, v = _rand((1, 2, 11, 5), 11), _rand((1, 2, 11, 3), 12)
+    r = O.fwd(q, k, v, scale=0.5)
+    assert np.allclose(r["o"], v.mean(axis=2, keepdims=True).repeat(7, axis=2), atol=1e-12, rtol=0)
+    assert np.allclose(r["lse"], math.log(11), atol=1e-12, rtol=0)
+
+
+def test_causal_zero_query_gives_prefix_means():
+    q = np.zeros((1, 1, 9, 4))
+    k, v = _rand((1, 1, 9, 4), 13), _rand((1, 1, 9, 3), 14)
+    r = O.fwd(q, k, v, scale=0.5, causal=True)
+    want = np.cumsum(v, axis=2) / np.arange(1, 10)[None, None, :, None]
+    assert np.allclose(r["o"], want, atol=1e-12, rtol=0)
+    assert np.allclose(r["lse"][0, 0], np.log(np.arange(1, 10)), atol=1e-12, rtol=0)
+    # row 0 sees only key 0
+    assert np.allclose(r["o"][0, 0, 0], v[0, 0, 0], atol=1e-15)
+
+
+def test_causal_with_more_keys_than_queries_is_top_left():
+    q, k, v = _rand((1, 1, 4, 3), 15), _rand((1, 1, 9, 3), 16), _rand((1, 1, 9, 2), 17)
+    r = O.fwd(q, k, v, scale=1.0, causal=True)
+    # row i of a top-left causal mask sees keys 0..i only
+    for i in range(4):
+        sub = O.fwd(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], scale=1.0)
+        assert np.allclose(r["o"][0, 0, i], sub["o"][0, 0, 0], atol=1e-14)
+
+
+def test_key_permutation_invariance():
+    q, k, v = _rand((1, 2, 13, 6), 18), _rand((1, 2, 17, 6), 19), _rand((1, 2, 17, 5), 20)
+    perm = np.random.default_rng(21).permutation(17)
+    a = O.fwd(q, k, v, scale=0.4)
+    b = O.fwd(q, k[:, :, perm], v[:, :, perm], scale=0.4)
+    assert np.allclose(a["o"], b["o"], atol=1e-12, rtol=0)
+    assert np.allclose(a["lse"], b["lse"], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_forward_matches_torch_sdpa_float64(causal, with_bias):
+    B, H, Sq, Skv, Dq, Dv = 2, 3, 19, 23 if not causal else 19, 7, 5
+    q, k, v = _rand((B, H, Sq, Dq), 22), _rand((B, H, Skv, Dq), 23), _rand((B, H, Skv, Dv), 24)
+    bias = _rand((B, H, Sq, Skv), 25) if with_bias else None
+    scale = 0.37
+    r = O.fwd(q, k, v, scale=scale, causal=causal, bias=bias)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    mask = None
+    if with_bias:
+        mask = torch.from_numpy(bias)
+    if causal and with_bias:
+        tri = torch.ones(Sq, Skv, dtype=torch.bool).tril()
+        mask = mask.masked_fill(~tri, float("-inf"))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    else:
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                               is_causal=causal, scale=scale)
+    assert np.allclose(r["o"], ref.numpy(), atol=1e-12, rtol=0)
+    s = scale * torch.einsum("bhid,bhjd->bhij", tq, tk)
+    if with_bias:
+        s = s + torch.from_numpy(bias)
+    if causal:
+        s = s.masked_fill(~torch.ones(Sq, Skv, dtype=torch.bool).tril(), float("-inf"))
+    assert np.allclose(r["lse"], torch.logsumexp(s, -1).numpy(), atol=1e-12, rtol=0)
+
+
+def test_dropout_applies_scaled_keep_mask_after_normalisation():
+    B, H, S, D = 1, 2, 21, 6
+    q, k, v = _rand((B, H, S, D), 26), _rand((B, H, S, D), 27), _rand((B, H, S, D), 28)
+    p = 0.3
+    r = O.fwd(q, k, v, scale=0.5, causal=True, p_drop=p, seed=99, offset=3, want_keep=True)
+    plain = O.fwd(q, k, v, scale=0.5, causal=True)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    s = 0.5 * torch.einsum("bhid,bhjd->bhij", tq, tk)
+    s = s.masked_fill(~torch.ones(S, S, dtype=torch.bool).tril(), float("-inf"))
+    P = torch.softmax(s, -1)
+    keep = torch.from_numpy(r["keep"].astype(np.float64))
+    z = keep / (1.0 - np.float64(np.float32(p)))
+    assert np.allclose(r["o"], (P * z @ tv).numpy(), atol=1e-12, rtol=0)
+    assert np.array_equal(r["lse"], plain["lse"])  # LSE from the undropped P
+
+
+# ------------------------------------------------------ backward pins -------
+def _loss(q, k, v, dout, bias, **kw):
+    return float(np.sum(O.fwd(q, k, v, bias=bias, **kw)["o"] * dout))
+
+
+@pytest.mark.parametrize("causal,with_bias,p", [(False, False, 0.0), (True, False, 0.0),
+                                                 (False, True, 0.0), (True, True, 0.25)])
+def test_backward_central_differences(causal, with_bias, p):
+    B, H, Sq, Skv, Dq, Dv = 1, 2, 5, 7 if not causal else 5, 3, 4
+    q, k, v = _rand((B, H, Sq, Dq), 30), _rand((B, H, Skv, Dq), 31), _rand((B, H, Skv, Dv), 32)
+    dout = _rand((B, H, Sq, Dv), 33)
+    bias = _rand((B, H, Sq, Skv), 34) if with_bias else None
+    kw = dict(scale=0.6, causal=causal, p_drop=p, seed=5, offset=0)
+    g = O.bwd(q, k, v, dout, bias=bias, **kw)
+    eps = 1e-6
+    targets = [("dq", q), ("dk", k), ("dv", v)] + ([("dbias", bias)] if with_bias else [])
+    for name, x in targets:
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, dout, bias, **kw)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, dout, bias, **kw)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(num - g[name])) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("causal,with_bias,p", [(False, True, 0.0), (True, False, 0.0),
+                                                 (True, True, 0.2)])
+def test_backward_matches_torch_autograd_float64(causal, with_bias, p):
+    B, H, Sq, Skv, Dq, Dv = 2, 2, 11, 13 if not causal else 11, 5, 4
+    q, k, v = _rand((B, H, Sq, Dq), 40), _rand((B, H, Skv, Dq), 41), _rand((B, H, Skv, Dv), 42)
+    dout = _rand((B, H, Sq, Dv), 43)
+    bias = _rand((B, H, Sq, Skv), 44) if with_bias else None
+    scale = 0.45
+    kw = dict(scale=scale, causal=causal, p_drop=p, seed=77, offset=9)
+    g = O.bwd(q, k, v, dout, bias=bias, **kw)
+    keep = O.fwd(q, k, v, bias=bias, want_keep=True, **kw)["keep"] if p > 0 else None
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    tb = torch.tensor(bias, requires_grad=True) if with_bias else None
+    s = scale * tq @ tk.transpose(-1, -2)
+    if with_bias:
+        s = s + tb
+    if causal:
+        s = s.masked_fill(~torch.ones(Sq, Skv, dtype=torch.bool).tril(), float("-inf"))
+    P = torch.softmax(s, -1)
+    if p > 0:
+        P = P * (torch.from_numpy(keep.astype(np.float64)) / (1.0 - np.float64(np.float32(p))))
+    out = P @ tv
+    out.backward(torch.from_numpy(dout))
+    assert np.allclose(g["o"], out.detach().numpy(), atol=1e-12, rtol=0)
+    assert np.allclose(g["dq"], tq.grad.numpy(), atol=1e-10, rtol=0)
+    assert np.allclose(g["dk"], tk.grad.numpy(), atol=1e-10, rtol=0)
+    assert np.allclose(g["dv"], tv.grad.numpy(), atol=1e-10, rtol=0)
+    if with_bias:
+        assert np.allclose(g["dbias"], tb.grad.numpy(), atol=1e-10, rtol=0)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_backward_invariants(p):
+    B, H, S, D = 1, 3, 29, 8
+    q, k, v, dout = (_rand((B, H, S, D), 50 + i) for i in range(4))
+    bias = _rand((B, H, S, S), 55)
+    g = O.bwd(q, k, v, dout, bias=bias, scale=0.3, causal=True, p_drop=p, seed=3)
+    # softmax shift invariance: every row of dS sums to zero
+    assert np.allclose(g["dbias"].sum(-1), 0.0, atol=1e-12)
+    # hence sum over keys of dK vanishes
+    assert np.allclose(g["dk"].sum(2), 0.0, atol=1e-11)
+    if p == 0.0:
+        # rows of P sum to one: sum_j dV_j = sum_i dO_i
+        assert np.allclose(g["dv"].sum(2), dout.sum(2), atol=1e-11)
+    # D from the backward equals rowsum(dO o O) with O from the forward
+    f = O.fwd(q, k, v, bias=bias, scale=0.3, causal=True, p_drop=p, seed=3)
+    assert np.allclose(g["D"], np.sum(dout * f["o"], -1), atol=1e-12, rtol=0)
+    assert np.allclose(g["lse"], f["lse"], atol=0, rtol=0)
+
+
+# ------------------------------------------------------------ group mode ----
+def test_group_mode_equals_batch_mode_per_sequence():
+    H, D = 2, 6
+    lens = [5, 1, 12, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    q, k, v, dout = (_rand((T, H, D), 60 + i) for i in range(4))
+    kw = dict(scale=0.5, causal=True, p_drop=0.2, seed=11, offset=2)
+    gf = O.fwd(q, k, v, cu_seqlens_q=cu, cu_seqlens_kv=cu, **kw)
+    gb = O.bwd(q, k, v, dout, cu_seqlens_q=cu, cu_seqlens_kv=cu, **kw)
+    for n, L in enumerate(lens):
+        sl = slice(cu[n], cu[n + 1])
+        def bhsd(x):
+            return np.ascontiguousarray(x[sl].transpose(1, 0, 2))[None]
+        # the batch-mode run of one sequence must use batch index n for the RNG:
+        # build a batch of n+1 copies and read entry n
+        rep = lambda x: np.repeat(bhsd(x), n + 1, axis=0)
+        bf = O.fwd(rep(q), rep(k), rep(v), heads=[(n, h) for h in range(H)], **kw)
+        bb = O.bwd(rep(q), rep(k), rep(v), rep(dout), heads=[(n, h) for h in range(H)], **kw)
+        assert np.array_equal(gf["o"][sl].transpose(1, 0, 2), bf["o"][n])
+        assert np.array_equal(gf["lse"][:, sl], bf["lse"][n])
+        for name in ("dq", "dk", "dv"):
+            assert np.array_equal(gb[name][sl].transpose(1, 0, 2), bb[name][n])
+
+
+# --------------------------------------------------------- mutation check ----
+MUTANTS = {
+    # a dropped bias term
+    "bias": ("+ (h->bias ? h->bias[i * h->ld_bias + j] : 0.0)", ""),
+    # an off-by-one causal boundary
+    "causal": ("if (h->causal && i < last) last = i;", "if (h->causal && i < last) last = i - 1;"),
+    # a wrong sign in dS
+    "dS": ("double dS = s[j] * (z[j] * dot - D);", "double dS = s[j] * (z[j] * dot + D);"),
+    # a transposed operand in dK
+    "dK": ("dkj[c] += h->scale * dS * qi[c];", "dkj[c] += h->scale * dS * kj[c];"),
+    # dropout rescale forgotten
+    "rescale": ("double rescale = 1.0 / (1.0 - (double)h->p_drop);", "double rescale = 1.0;"),
+    # a wrong Philox word order
+    "philox": ("uint32_t n1 = lo1;", "uint32_t n1 = lo0;"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_oracle_mistakes(mutant, tmp_path):
+    """Build a deliberately broken copy of the oracle and check that at least
+    one of the pins above fails against it."""
+    src = open(os.path.join(ROOT, "oracle", "sdpa_oracle.c")).read()
+    old, new = MUTANTS[mutant]
+    assert old in src
+    mdir = tmp_path / "oracle"
+    mdir.mkdir()
+    (mdir / "sdpa_oracle.c").write_text(src.replace(old, new))
+    for f in ("sdpa_oracle.py", "__init__.py", "build.py"):
+        shutil.copy(os.path.join(ROOT, "oracle", f), mdir / f)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+                    str(mdir / "sdpa_oracle.c"), "-o", str(mdir / "liboracle.so"), "-lm"],
+                   check=True)
+    code = (
+        "import sys; sys.path.insert(0, %r); sys.path.insert(1, %r)\n"
+        "import oracle.sdpa_oracle as O; assert O.__file__.startswith(%r)\n"
+        "import tests.test_oracle_pins as T\n"
+        "T.O = O\n"
+        "import inspect\n"
+        "fails = 0\n"
+        "for name, fn in sorted(vars(T).items()):\n"
+        "    if not name.startswith('test_') or name == 'test_pins_catch_planted_oracle_mistakes':\n"
+        "        continue\n"
+        "    if name == 'test_philox_matches_rocrand_engine':\n"
+        "        continue\n"
+        "    params = getattr(fn, 'pytestmark', [])\n"
+        "    combos = [()]\n"
+        "    for m in params:\n"
+        "        if m.name == 'parametrize':\n"
+        "            names = [n.strip() for n in m.args[0].split(',')]\n"
+        "            combos = [c + (dict(zip(names, v if isinstance(v, tuple) else (v,))),) for c in combos for v in m.args[1]]\n"
+        "    for c in combos:\n"
+        "        kw = {}\n"
+        "        for d in c: kw.update(d)\n"
+        "        try:\n"
+        "            fn(**kw)\n"
+        "        except Exception:\n"
+        "            fails += 1\n"
+        "print('FAILS', fails)\n"
+    ) % (str(tmp_path), ROOT, str(mdir))
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
+    assert "FAILS" in r.stdout, r.stderr[-2000:]
+    n = int(r.stdout.split("FAILS")[1].split()[0])
+    assert n > 0, f"no pin caught the planted mistake {mutant!r}"
