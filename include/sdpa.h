@@ -1,0 +1,182 @@
+/*
+ * sdpa.h - C ABI of the fused scaled dot-product attention library for
+ * AMD Instinct MI355X (gfx950).  Forward and backward of multi-head
+ * attention with optional additive bias, top-left causal mask, Philox
+ * dropout and packed variable-length (group) mode.
+ *
+ * The operation (Composable Kernel, "fmha_bwd_kernel.hpp Source File",
+ * the formula comment at the head of the file):
+ *   S   = scale * Q K^T            S'' = S + Bias        P = softmax_row(S'')
+ *   O   = (P o Z) V                LSE = row log-sum-exp of S'' (natural log)
+ *   D   = rowsum(dO o O)           dV  = (P o Z)^T dO    dP = (dO V^T) o Z
+ *   dS  = P o (dP - D)             dBias = dS
+ *   dQ  = scale * dS K             dK  = scale * dS^T Q
+ * where Z is the dropout keep mask scaled by 1/(1-p) (Z = 1 when p = 0).
+ *
+ * The argument list follows the problem statement of PyTorch's cuDNN
+ * attention glue ("MHA.cpp", run_cudnn_SDP_fprop / run_cudnn_SDP_bprop):
+ * b, h, s_q, s_kv, d_qk, d_v, scaling_factor, is_causal,
+ * dropout_probability, q, k, v, optional attn_bias, softmax stats, o,
+ * dropout seed and offset.  Group mode follows CK's seqstart_q / seqstart_k
+ * kernel arguments (FmhaBwdDQDKDVKernel group-mode kargs).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates no memory and keeps no per-call state; calls are
+ *     thread-safe.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns before it completes.
+ *   - Errors are status codes; nothing is thrown across the ABI.  On error,
+ *     sdpa_last_error_message() returns a thread-local description.
+ *     Validation happens before anything is enqueued, so an error other than
+ *     SDPA_ERR_HIP means no work was launched.
+ *   - Any of b, h, s_q, s_kv equal to 0 is a successful no-op (PyTorch's
+ *     cuDNN glue returns early on zero-element tensors).
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDPA_OK = 0,
+    SDPA_ERR_INVALID_ARG = 1, /* malformed arguments (null, negative, bad stride) */
+    SDPA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (head dim, combination) */
+    SDPA_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned */
+    SDPA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} sdpa_status_t;
+
+/* io element type of Q, K, V, O, dO, dQ, dK, dV, bias and dBias.
+ * LSE, D and all accumulation are fp32 whatever the io type (the cuDNN glue
+ * fixes fp32 "intermediate" and "compute" types and fp32 stats). */
+typedef enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2 } sdpa_dtype_t;
+
+/* Element strides of a 4-D attention tensor.  The innermost dimension
+ * (head dim, or s_kv for the bias) always has stride 1.
+ *   batch mode : element (b, h, s, d) is at  b*batch + h*head + s*seq + d
+ *   group mode : element (token t, h, d) is at  h*head + t*seq + d; `batch`
+ *                is ignored (tokens of all sequences are packed). */
+typedef struct {
+    int64_t batch, head, seq;
+} sdpa_strides_t;
+
+typedef struct {
+    uint32_t struct_size;       /* must be sizeof(sdpa_problem_t) */
+    sdpa_dtype_t dtype;
+    int64_t b;                  /* batch; group mode: number of sequences */
+    int64_t h;                  /* heads (query and key/value heads are equal) */
+    int64_t s_q, s_kv;          /* sequence lengths; group mode: the maxima */
+    int64_t d_qk, d_v;          /* head dims of Q/K and of V/O */
+    float scaling_factor;       /* multiplies Q K^T; the bias is added after it */
+    int32_t is_causal;          /* top-left causal: key j visible from query i iff j <= i */
+    float dropout_probability;  /* 0 <= p < 1 */
+    uint64_t dropout_seed;      /* Philox key */
+    uint64_t dropout_offset;    /* Philox counter word 3 (low 32 bits used) */
+    /* Optional device pointer to {seed, offset} (two uint64); when non-null
+     * it replaces dropout_seed / dropout_offset (CK passes either values or
+     * device pointers: FmhaBwdDropoutSeedOffset). */
+    const uint64_t *dropout_seed_offset_dev;
+    /* Group (varlen) mode: device int32 arrays of length b+1 holding the
+     * first token of each sequence (cu_seqlens; CK's seqstart_q_ptr /
+     * seqstart_k_ptr).  Both null = batch mode; both non-null = group mode.
+     * The host reads no element of them: s_q and s_kv must bound every
+     * sequence length. */
+    const int32_t *cu_seqlens_q;
+    const int32_t *cu_seqlens_kv;
+} sdpa_problem_t;
+
+/* Dropout keep mask (the library's own specification; the pages give the
+ * ingredients - an 8-bit threshold and a 1/(1-p) rescale in CK's
+ * init_dropout, seed and offset in cuDNN's graph - but no generator):
+ *   counter = (j >> 2, i >> 2, b*h_count + h, low32(offset)),
+ *   key     = (low32(seed), high32(seed)),
+ *   r       = Philox4x32-10(counter, key)   (Salmon et al., SC'11),
+ *   byte    = (r[i & 3] >> (8 * (j & 3))) & 0xff,
+ *   keep    = byte >= round(256 p);  kept values are scaled by 1/(1-p).
+ * i, j are query and key positions within the sequence; in group mode b is
+ * the sequence index. */
+
+/* ------------------------------------------------------------------------ */
+/* Workspace.  Bytes of device scratch the caller must pass to sdpa_fwd /    */
+/* sdpa_bwd (the cuDNN glue allocates a workspace per call; the oneDNN       */
+/* backward sizes its scratchpad for D).  Returns 0 when none is needed and  */
+/* also 0 for a problem that fails validation.  Alignment: 256 bytes.        */
+/* ------------------------------------------------------------------------ */
+size_t sdpa_fwd_workspace_size(const sdpa_problem_t *problem);
+size_t sdpa_bwd_workspace_size(const sdpa_problem_t *problem);
+
+/* Forward (run_cudnn_SDP_fprop's contract).
+ *   q [b,h,s_q,d_qk]  k [b,h,s_kv,d_qk]  v [b,h,s_kv,d_v]  o [b,h,s_q,d_v]
+ *     (group mode: [T,h,d]; the strides say where each element is).
+ *   attn_bias: nullable, [b,h,s_q,s_kv] with its own strides (batch mode
+ *     only); added to the scaled scores before the softmax.
+ *   softmax_lse: nullable fp32.  Batch mode: dense [b,h,s_q]; group mode:
+ *     dense [h,T_q] (CK addresses LSE as head*T + token).  Null means
+ *     inference: no stats are written.
+ *   dropout_keep_out: nullable debug output, dense uint8 [b,h,s_q,s_kv]
+ *     (batch mode only): 1 where the element was kept.  Positions the causal
+ *     mask hides are left unwritten.
+ * Errors: SDPA_ERR_INVALID_ARG for null tensors, bad strides, p outside
+ * [0,1) or half the varlen pair; SDPA_ERR_UNSUPPORTED for head dims outside
+ * the compiled set (16-bit io: d_qk in {64,128,192}, d_v in {64,128};
+ * fp32: d_qk, d_v <= 256), bias in group mode, keep output in group mode. */
+sdpa_status_t sdpa_fwd(const sdpa_problem_t *problem,
+                       const void *q, sdpa_strides_t q_strides,
+                       const void *k, sdpa_strides_t k_strides,
+                       const void *v, sdpa_strides_t v_strides,
+                       const void *attn_bias, sdpa_strides_t bias_strides,
+                       void *o, sdpa_strides_t o_strides,
+                       float *softmax_lse,
+                       uint8_t *dropout_keep_out,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Backward (run_cudnn_SDP_bprop's contract).  Consumes the forward's o and
+ * softmax_lse (same layout as written by sdpa_fwd) and the same seed,
+ * offset and probability.  Writes dq, dk, dv (shapes of q, k, v, each with
+ * its own strides) and, when non-null, dbias (shape of the bias; requires
+ * attn_bias).  Results are deterministic: bitwise identical from run to run.
+ * workspace must hold sdpa_bwd_workspace_size(problem) bytes.
+ * Errors as for sdpa_fwd, plus SDPA_ERR_WORKSPACE. */
+sdpa_status_t sdpa_bwd(const sdpa_problem_t *problem,
+                       const void *q, sdpa_strides_t q_strides,
+                       const void *k, sdpa_strides_t k_strides,
+                       const void *v, sdpa_strides_t v_strides,
+                       const void *attn_bias, sdpa_strides_t bias_strides,
+                       const void *o, sdpa_strides_t o_strides,
+                       const void *d_o, sdpa_strides_t do_strides,
+                       const float *softmax_lse,
+                       void *dq, sdpa_strides_t dq_strides,
+                       void *dk, sdpa_strides_t dk_strides,
+                       void *dv, sdpa_strides_t dv_strides,
+                       void *dbias, sdpa_strides_t dbias_strides,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Backward preprocess alone: D = rowsum(dO o O) in fp32 (CK's
+ * FmhaBwdOGradDotOKernel; oneDNN's backward "preprocess" kernel), written
+ * densely as [b,h,s_q] (group mode [h,T_q]).  sdpa_bwd runs it itself; it is
+ * exported for testing and measurement. */
+sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t *problem,
+                                  const void *o, sdpa_strides_t o_strides,
+                                  const void *d_o, sdpa_strides_t do_strides,
+                                  float *d_out, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *sdpa_status_string(sdpa_status_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *sdpa_last_error_message(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

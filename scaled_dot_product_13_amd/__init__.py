@@ -1,0 +1,17 @@
+"""Fused scaled dot-product attention (forward + backward) for MI355X / gfx950.
+
+The compute lives in libsdpa.so (hand-written HIP kernels behind the C ABI of
+include/sdpa.h); `scaled_dot_product_13_amd.sdpa` is its ctypes binding.  The
+binding is imported lazily so that `scaled_dot_product_13_amd.build` can run
+before the library exists; touching any API name without a built library
+raises ImportError (there is no fallback path).
+"""
+_API = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_preprocess", "make_problem", "SdpaError",
+        "version", "Problem", "Strides")
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import sdpa as _s
+        return getattr(_s, name)
+    raise AttributeError(name)

@@ -1,0 +1,312 @@
+// Host side of the C ABI declared in include/sdpa.h: argument validation,
+// workspace sizing and kernel launches on the caller's stream.
+//
+// Behaviour taken from the pages' host drivers:
+//   - zero-element problems return success without launching (PyTorch
+//     "MHA.cpp", run_cudnn_SDP_fprop / run_cudnn_SDP_bprop early return);
+//   - the backward is a preprocess (D) plus main kernels, with a workspace
+//     the caller provides (oneDNN micro SDPA host driver, init_scratchpad and
+//     execute_backward; the cuDNN glue's workspace);
+//   - errors are reported as status codes with a message (oneDNN's status
+//     codes and VCHECK_SDPA_COND messages), never as exceptions.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/sdpa.h"
+#include "sdpa_params.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+sdpa_status_t fail(sdpa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  if (std::getenv("SDPA_LOG")) std::fprintf(stderr, "[sdpa] %s\n", g_msg);
+  return st;
+}
+
+bool log_on() {
+  static int on = std::getenv("SDPA_LOG") ? 1 : 0;
+  return on != 0;
+}
+
+size_t elem_size(sdpa_dtype_t t) { return t == SDPA_F32 ? 4 : 2; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+sdpa_status_t check_problem(const sdpa_problem_t* p) {
+  if (!p) return fail(SDPA_ERR_INVALID_ARG, "problem is null");
+  if (p->struct_size != sizeof(sdpa_problem_t))
+    return fail(SDPA_ERR_INVALID_ARG, "problem.struct_size is %u, expected %zu", p->struct_size,
+                sizeof(sdpa_problem_t));
+  if (p->dtype != SDPA_F32 && p->dtype != SDPA_F16 && p->dtype != SDPA_BF16)
+    return fail(SDPA_ERR_INVALID_ARG, "unknown dtype %d", (int)p->dtype);
+  if (p->b < 0 || p->h < 0 || p->s_q < 0 || p->s_kv < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "negative size (b=%lld h=%lld s_q=%lld s_kv=%lld)",
+                (long long)p->b, (long long)p->h, (long long)p->s_q, (long long)p->s_kv);
+  if (p->d_qk <= 0 || p->d_v <= 0)
+    return fail(SDPA_ERR_INVALID_ARG, "head dims must be positive (d_qk=%lld d_v=%lld)",
+                (long long)p->d_qk, (long long)p->d_v);
+  if (p->b > 65535 || p->h > 65535 || p->s_q > (1 << 30) || p->s_kv > (1 << 30))
+    return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the supported grid (b, h <= 65535)");
+  if (!(p->dropout_probability >= 0.f && p->dropout_probability < 1.f))
+    return fail(SDPA_ERR_INVALID_ARG, "dropout_probability %g outside [0, 1)",
+                (double)p->dropout_probability);
+  if (!std::isfinite(p->scaling_factor))
+    return fail(SDPA_ERR_INVALID_ARG, "scaling_factor is not finite");
+  if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
+    return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
+  if (p->dtype == SDPA_F32) {
+    if (p->d_qk > 256 || p->d_v > 256)
+      return fail(SDPA_ERR_UNSUPPORTED, "fp32 head dims must be <= 256 (d_qk=%lld d_v=%lld)",
+                  (long long)p->d_qk, (long long)p->d_v);
+    if (p->d_v % 4 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "fp32 d_v must be a multiple of 4");
+  } else if (!sdpa::mfma_dims_supported((int)p->d_qk, (int)p->d_v)) {
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "no 16-bit kernel for d_qk=%lld d_v=%lld (compiled: 64/64, 128/128, 192/128)",
+                (long long)p->d_qk, (long long)p->d_v);
+  }
+  return SDPA_OK;
+}
+
+bool empty_problem(const sdpa_problem_t* p) {
+  return p->b == 0 || p->h == 0 || p->s_q == 0 || p->s_kv == 0;
+}
+
+// A tensor operand: non-null, non-negative strides; for 16-bit io the
+// vectorised kernels need 16-byte aligned rows.
+sdpa_status_t check_tensor(const sdpa_problem_t* p, const void* ptr, sdpa_strides_t s,
+                           const char* name, bool need_vec) {
+  if (!ptr) return fail(SDPA_ERR_INVALID_ARG, "%s is null", name);
+  if (s.batch < 0 || s.head < 0 || s.seq < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "%s has a negative stride", name);
+  if (need_vec) {
+    size_t es = elem_size(p->dtype);
+    bool ok = ((uintptr_t)ptr % 16 == 0) && (s.head * es) % 16 == 0 && (s.seq * es) % 16 == 0 &&
+              (p->cu_seqlens_q || (s.batch * es) % 16 == 0);
+    if (!ok)
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "%s: base pointer and batch/head/seq strides must be multiples of 16 bytes", name);
+  }
+  return SDPA_OK;
+}
+
+sdpa::Str to_str(sdpa_strides_t s) { return sdpa::Str{s.batch, s.head, s.seq}; }
+
+void fill_dropout(const sdpa_problem_t* p, sdpa::DropoutArgs& d) {
+  float pr = p->dropout_probability;
+  d.enabled = pr > 0.f ? 1 : 0;
+  double t = std::floor(256.0 * (double)pr + 0.5);
+  if (t > 255.0) t = 255.0;
+  d.threshold = (uint32_t)t;
+  d.rescale = pr > 0.f ? (float)(1.0 / (1.0 - (double)pr)) : 1.f;
+  d.seed = p->dropout_seed;
+  d.offset = p->dropout_offset;
+  d.seed_offset_dev = p->dropout_seed_offset_dev;
+}
+
+sdpa::SeqInfo seq_info(const sdpa_problem_t* p) {
+  sdpa::SeqInfo s;
+  s.cu_q = p->cu_seqlens_q;
+  s.cu_kv = p->cu_seqlens_kv;
+  s.s_q = (int32_t)p->s_q;
+  s.s_kv = (int32_t)p->s_kv;
+  return s;
+}
+
+sdpa::IoType io(sdpa_dtype_t t) {
+  return t == SDPA_F32 ? sdpa::IoType::F32 : t == SDPA_F16 ? sdpa::IoType::F16 : sdpa::IoType::BF16;
+}
+
+bool bias_vec_ok(const sdpa_problem_t* p, const void* bias, sdpa_strides_t s) {
+  size_t es = elem_size(p->dtype);
+  return bias && (uintptr_t)bias % 16 == 0 && (s.batch * es) % 16 == 0 &&
+         (s.head * es) % 16 == 0 && (s.seq * es) % 16 == 0;
+}
+
+size_t d_workspace_bytes(const sdpa_problem_t* p) {
+  return align_up(sizeof(float) * (size_t)p->b * (size_t)p->h * (size_t)p->s_q);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdpa_version(void) { return "0.1.0"; }
+
+const char* sdpa_status_string(sdpa_status_t st) {
+  switch (st) {
+    case SDPA_OK: return "SDPA_OK";
+    case SDPA_ERR_INVALID_ARG: return "SDPA_ERR_INVALID_ARG";
+    case SDPA_ERR_UNSUPPORTED: return "SDPA_ERR_UNSUPPORTED";
+    case SDPA_ERR_WORKSPACE: return "SDPA_ERR_WORKSPACE";
+    case SDPA_ERR_HIP: return "SDPA_ERR_HIP";
+  }
+  return "SDPA_ERR_UNKNOWN";
+}
+
+const char* sdpa_last_error_message(void) { return g_msg; }
+
+size_t sdpa_fwd_workspace_size(const sdpa_problem_t* p) {
+  (void)p;
+  return 0;
+}
+
+size_t sdpa_bwd_workspace_size(const sdpa_problem_t* p) {
+  if (check_problem(p) != SDPA_OK || empty_problem(p)) return 0;
+  return d_workspace_bytes(p);
+}
+
+sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s, const void* k,
+                       sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
+                       const void* attn_bias, sdpa_strides_t bias_s, void* o, sdpa_strides_t o_s,
+                       float* softmax_lse, uint8_t* dropout_keep_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;
+  if (empty_problem(p)) return SDPA_OK;
+  const bool vec = p->dtype != SDPA_F32;
+  if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, v, v_s, "v", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, o, o_s, "o", vec)) != SDPA_OK) return st;
+  const bool group = p->cu_seqlens_q != nullptr;
+  if (attn_bias) {
+    if (group) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
+    if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
+  }
+  if (dropout_keep_out && group)
+    return fail(SDPA_ERR_UNSUPPORTED, "dropout_keep_out is only available in batch mode");
+
+  sdpa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o;
+  a.lse = softmax_lse;
+  a.keep = p->dropout_probability > 0.f ? dropout_keep_out : nullptr;
+  a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s);
+  a.sb_ = to_str(bias_s); a.so_ = to_str(o_s);
+  a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
+  a.B = (int32_t)p->b; a.H = (int32_t)p->h;
+  a.seq = seq_info(p);
+  a.scale = p->scaling_factor;
+  a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
+  fill_dropout(p, a.drop);
+  if (log_on())
+    std::fprintf(stderr, "[sdpa] fwd dtype=%d b=%lld h=%lld s_q=%lld s_kv=%lld d=%lld/%lld causal=%d "
+                 "bias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b, (long long)p->h,
+                 (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk, (long long)p->d_v,
+                 p->is_causal, attn_bias != nullptr, (double)p->dropout_probability, group);
+  hipError_t e = sdpa::launch_fwd(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
+  a.B = (int32_t)p->b; a.H = (int32_t)p->h;
+  a.seq = seq_info(p);
+  a.scale = p->scaling_factor;
+  a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
+  fill_dropout(p, a.drop);
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t* p, const void* o, sdpa_strides_t o_s,
+                                  const void* d_o, sdpa_strides_t do_s, float* d_out,
+                                  void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
+  if (!d_out) return fail(SDPA_ERR_INVALID_ARG, "d_out is null");
+  if (p->d_v % (16 / (int)elem_size(p->dtype)) != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "d_v must fill whole 16-byte chunks");
+  sdpa::BwdArgs a{};
+  fill_bwd_args(p, a);
+  a.o = o; a.dout = d_o; a.so_ = to_str(o_s); a.sdo_ = to_str(do_s);
+  a.dvec = d_out;
+  hipError_t e = sdpa::launch_bwd_pre(io(p->dtype), (int)p->d_v, a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "preprocess launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s, const void* k,
+                       sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
+                       const void* attn_bias, sdpa_strides_t bias_s, const void* o,
+                       sdpa_strides_t o_s, const void* d_o, sdpa_strides_t do_s,
+                       const float* softmax_lse, void* dq, sdpa_strides_t dq_s, void* dk,
+                       sdpa_strides_t dk_s, void* dv, sdpa_strides_t dv_s, void* dbias,
+                       sdpa_strides_t dbias_s, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  const bool vec = p->dtype != SDPA_F32;
+  if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, v, v_s, "v", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, dq, dq_s, "dq", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, dk, dk_s, "dk", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, dv, dv_s, "dv", vec)) != SDPA_OK) return st;
+  if (!softmax_lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null (the backward needs the stats)");
+  const bool group = p->cu_seqlens_q != nullptr;
+  if (attn_bias) {
+    if (group) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
+    if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
+  }
+  if (dbias) {
+    if (!attn_bias) return fail(SDPA_ERR_INVALID_ARG, "dbias requires attn_bias");
+    if ((st = check_tensor(p, dbias, dbias_s, "dbias", false)) != SDPA_OK) return st;
+  }
+  if (p->d_v % (16 / (int)elem_size(p->dtype)) != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "d_v must fill whole 16-byte chunks");
+  const size_t need = d_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16 != 0)
+    return fail(SDPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  sdpa::BwdArgs a{};
+  fill_bwd_args(p, a);
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o; a.dout = d_o;
+  a.lse = softmax_lse;
+  a.dvec = (float*)workspace;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbias = dbias;
+  a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
+  a.so_ = to_str(o_s); a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s); a.sdk_ = to_str(dk_s);
+  a.sdv_ = to_str(dv_s); a.sdb_ = to_str(dbias_s);
+  a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  const sdpa::IoType t = io(p->dtype);
+  const bool causal = p->is_causal != 0;
+  if (log_on())
+    std::fprintf(stderr, "[sdpa] bwd dtype=%d b=%lld h=%lld s_q=%lld s_kv=%lld d=%lld/%lld causal=%d "
+                 "bias=%d dbias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b,
+                 (long long)p->h, (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk,
+                 (long long)p->d_v, p->is_causal, attn_bias != nullptr, dbias != nullptr,
+                 (double)p->dropout_probability, group);
+  hipError_t e = sdpa::launch_bwd_pre(t, (int)p->d_v, a, s);
+  if (e == hipSuccess) e = sdpa::launch_bwd_dkdv(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+  if (e == hipSuccess) e = sdpa::launch_bwd_dq(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+}  // extern "C"

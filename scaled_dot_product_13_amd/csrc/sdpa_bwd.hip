@@ -1,0 +1,675 @@
+// Backward attention kernels for gfx950.
+//
+// What is computed (Composable Kernel "fmha_bwd_kernel.hpp Source File",
+// formula comment dV, dP, D, dS'', dBias, dK, dQ):
+//   D = rowsum(dO o O);  P = exp(S'' - LSE) recomputed from the saved stats;
+//   dV = (P o Z)^T dO;  dP = (dO V^T) o Z;  dS = P o (dP - D);  dBias = dS;
+//   dK = scale dS^T Q;  dQ = scale dS K.
+//
+// Three kernels, all deterministic (no atomics, every output element owned
+// and written by exactly one workgroup, every sum in a fixed order):
+//   bwd_pre   D = rowsum(dO o O) in fp32 - the separate preprocess of CK
+//             (FmhaBwdOGradDotOKernel) and of oneDNN's execute_backward.
+//   dkdv_*    key-stationary: one workgroup per 128 keys of a (batch, head)
+//             (the grid of CK's GridSize and of oneDNN's backward main
+//             kernel) keeps K and V in registers and accumulates dK, dV over
+//             all query tiles; it also writes dBias.
+//   dq_*      query-stationary: one workgroup per 128 query rows recomputes
+//             S and dP for its rows and accumulates dQ in registers over all
+//             key tiles, in ascending key order.
+// Splitting dQ off trades two recomputed products (S and dP) for a dQ
+// reduction with no workspace, no atomics and no inter-workgroup waiting;
+// CK instead writes one fp32 dQ slice per key tile and sums the slices in
+// FmhaBwdConvertQGradKernel, and oneDNN adds fp32 dQ atomically.
+#include "sdpa_kcommon.h"
+
+namespace sdpa {
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO o O): 16 lanes per row, 16-byte loads, fp32 accumulation.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int b = blockIdx.z, h = blockIdx.y;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int sub = threadIdx.x & 15;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool ok = row < sp.sq;
+  float acc = 0.f;
+  if (ok) {
+    const T* o = base_ptr<T>(a.o, a.so_, sp, h, true) + (int64_t)row * a.so_.s;
+    const T* d = base_ptr<T>(a.dout, a.sdo_, sp, h, true) + (int64_t)row * a.sdo_.s;
+    for (int c = sub; c * EPC < dv; c += 16) {
+      u32x4 x = *(const u32x4*)(o + c * EPC);
+      u32x4 y = *(const u32x4*)(d + c * EPC);
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += __uint_as_float(x[e]) * __uint_as_float(y[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += to_f32<T>((uint16_t)(x[e] & 0xffffu)) * to_f32<T>((uint16_t)(y[e] & 0xffffu));
+          acc += to_f32<T>((uint16_t)(x[e] >> 16)) * to_f32<T>((uint16_t)(y[e] >> 16));
+        }
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 8, 16);
+  acc += __shfl_xor(acc, 4, 16);
+  acc += __shfl_xor(acc, 2, 16);
+  acc += __shfl_xor(acc, 1, 16);
+  if (ok && sub == 0) {
+    int64_t base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+    a.dvec[base + row] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (and dBias).  Workgroup = 4 waves x 32 keys; query tiles of 64.
+// Per wave and query tile, with the queries fetched in sig order:
+//   S  = Q K^T   (A = Q rows from LDS, B = K^T in registers)
+//   dP = dO V^T  (A = dO rows from LDS, B = V^T in registers)
+// The accumulators hold one key per lane, so P and dS feed
+//   dV^T += dO^T (P o Z)   and   dK^T += Q^T dS
+// directly as B operands; the A operands dO^T and Q^T come from the same LDS
+// tiles through the transposing LDS read.
+template <int DQK, int DV, bool DROP> struct DkdvOcc {
+  static constexpr int value = 1;
+};
+
+template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
+  constexpr int BC = 128, BQ = 64;
+  constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
+  // double-buffered Q, dO, LSE and D tiles, plus (aligned bias) the bias tile
+  __shared__ __attribute__((aligned(1024))) T sQ[2][BQ * DQK];
+  __shared__ __attribute__((aligned(1024))) T sO[2][BQ * DV];
+  __shared__ __attribute__((aligned(1024))) T sB[BIAS ? 2 : 1][BIAS ? BQ * BC : 64];
+  __shared__ __attribute__((aligned(256))) float sL[2][BQ], sD[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int sq = sp.sq, skv = sp.skv;
+  const int kv0 = blockIdx.x * BC;
+  if (kv0 >= skv) return;
+
+  const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
+  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
+  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
+  const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
+  const int64_t lse_base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+  const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+  const uint16_t* bg = nullptr;
+  uint16_t* dbg = nullptr;
+  if (BIAS) {
+    bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+    if (a.dbias) dbg = (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
+  }
+
+  const int kvr = kv0 + 32 * w + l32;  // this lane's key
+  const bool kv_ok = kvr < skv;
+  u32x4 kreg[KT], vreg[VT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    kreg[t] = kv_ok ? *(const u32x4*)(kg + (int64_t)kvr * a.sk_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < VT; ++t)
+    vreg[t] = kv_ok ? *(const u32x4*)(vg + (int64_t)kvr * a.sv_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+
+  DropKey dk{};
+  const uint32_t bh = (uint32_t)(b * a.H + h);
+  if (DROP) dk = drop_key(a.drop);
+  const float rescale = DROP ? a.drop.rescale : 1.f;
+
+  f32x16 dkacc[QB], dvacc[VB];
+#pragma unroll
+  for (int i = 0; i < QB; ++i) dkacc[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < VB; ++i) dvacc[i] = f32x16{};
+
+  // causal: query rows below kv0 see none of these keys
+  const int q_begin = CAUSAL ? (kv0 / BQ) * BQ : 0;
+  if (CAUSAL && dbg && kv_ok) {
+    // dBias is zero wherever the mask hides the key: rows [0, q_begin)
+    for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+  }
+
+  // bias tiles come through LDS when the whole 64 x 128 tile is in range and
+  // its rows are 16-byte aligned; otherwise each lane reads its elements.
+  const bool bias_lds = BIAS && a.bias_vec && kv0 + BC <= skv;
+  const T* dog_ = dog;
+  const float* lseg = a.lse + lse_base;
+  const float* dvg = a.dvec + d_base;
+  auto issue = [&](int q0, int buf) {
+    tile_load_direct<DQK, BQ>(sQ[buf], qg, a.sq_.s, q0, sq, w, lane);
+    tile_load_direct<DV, BQ>(sO[buf], dog_, a.sdo_.s, q0, sq, w, lane);
+    if (BIAS && bias_lds)
+      tile_load_direct<BC, BQ>(sB[buf], (const T*)(bg + kv0), a.sb_.s, q0, sq, w, lane);
+    // the 64 fp32 LSE (wave 0) and D (wave 1) values, one row per lane,
+    // rows clamped to the sequence
+    if (w < 2) {
+      int r = q0 + lane;
+      r = r < sq ? r : sq - 1;
+      const float* src = (w == 0 ? lseg : dvg) + r;
+      float* dst = w == 0 ? sL[buf] : sD[buf];
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
+    }
+  };
+
+  if (q_begin < sq) issue(q_begin, 0);
+  int it = 0;
+  for (int q0 = q_begin; q0 < sq; q0 += BQ, ++it) {
+    const int buf = it & 1;
+    wait_all();
+    __syncthreads();
+    const T* cQ = sQ[buf];
+    const T* cO = sO[buf];
+    const float* cL = sL[buf];
+    const float* cD = sD[buf];
+    const T* cB = sB[BIAS ? buf : 0];
+    if (q0 + BQ < sq) issue(q0 + BQ, buf ^ 1);
+
+    // causal: this wave's keys are all above the last row of the tile
+    const bool active = kv0 + 32 * w < skv && (!CAUSAL || q0 + BQ - 1 >= kv0 + 32 * w);
+    if (!active) {
+      if (CAUSAL && dbg && kv_ok)  // the whole tile is hidden from my key
+        for (int i = q0 + g; i < min(q0 + BQ, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+      continue;
+    }
+
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 a0 = lds_rowA<DQK>(cQ, 0, 16 * t, lane);
+      u32x4 a1 = lds_rowA<DQK>(cQ, 32, 16 * t, lane);
+      s[0] = mfma32<T>(a0, kreg[t], s[0]);
+      s[1] = mfma32<T>(a1, kreg[t], s[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      u32x4 a0 = lds_rowA<DV>(cO, 0, 16 * t, lane);
+      u32x4 a1 = lds_rowA<DV>(cO, 32, 16 * t, lane);
+      dp[0] = mfma32<T>(a0, vreg[t], dp[0]);
+      dp[1] = mfma32<T>(a1, vreg[t], dp[1]);
+    }
+
+    uint32_t kw[8];
+    if (DROP) {
+      uint32_t var4[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
+      quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
+    }
+
+    const bool need_mask = (q0 + BQ > sq) || !kv_ok || (kv0 + 32 * w + 31 >= skv) ||
+                           (CAUSAL && q0 < kv0 + 32 * w + 31);
+    u32x4 pb[4], dsb[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = 32 * qb + 16 * (r >> 3) + 8 * g + (r & 7);  // local query row
+        const int qr = q0 + ql;
+        float x = s[qb][r] * a.scale_log2 - cL[ql] * kLog2e;
+        if (BIAS) {
+          float bval = 0.f;
+          if (bias_lds)
+            bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * w + l32)));
+          else if (kv_ok && qr < sq)
+            bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
+          x += bval * kLog2e;
+        }
+        const bool vis = !need_mask || (qr < sq && kv_ok && (!CAUSAL || kvr <= qr));
+        float p = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+        float z = 1.f, pz = p;
+        if (DROP) {
+          int k = 4 * qb + 2 * (r >> 3) + ((r & 7) >> 2);
+          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          z = keep ? rescale : 0.f;
+          pz = keep ? p : 0.f;
+        }
+        const float ds = vis ? p * (dp[qb][r] * z - cD[ql]) : 0.f;  // hidden: exactly 0
+        s[qb][r] = pz;
+        dp[qb][r] = ds;
+        if (BIAS && dbg && kv_ok && qr < sq) {
+          uint16_t bits = (uint16_t)(pack2<T>(ds, 0.f) & 0xffffu);
+          dbg[(int64_t)qr * a.sdb_.s + kvr] = bits;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      int qb = tt >> 1, r0 = 8 * (tt & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[tt][e] = pack2<T>(s[qb][r0 + 2 * e], s[qb][r0 + 2 * e + 1]);
+        dsb[tt][e] = pack2<T>(dp[qb][r0 + 2 * e], dp[qb][r0 + 2 * e + 1]);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        u32x4 av = lds_trA<DV>(cO, 16 * tt, 32 * vb, lane);
+        dvacc[vb] = mfma32<T>(av, pb[tt], dvacc[vb]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 aq = lds_trA<DQK>(cQ, 16 * tt, 32 * qb, lane);
+        dkacc[qb] = mfma32<T>(aq, dsb[tt], dkacc[qb]);
+      }
+    }
+  }
+
+  // epilogue: dK = scale * dK^T acc, dV = rescale * dV^T acc (one key per lane)
+  if (kv_ok) {
+    T* dkr = base_ptr_mut<T>(a.dk, a.sdk_, sp, h, false) + (int64_t)kvr * a.sdk_.s;
+    T* dvr = base_ptr_mut<T>(a.dv, a.sdv_, sp, h, false) + (int64_t)kvr * a.sdv_.s;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int d = 32 * qb + 8 * rr + 4 * g;
+        u32x2 v2;
+        v2[0] = pack2<T>(dkacc[qb][4 * rr] * a.scale, dkacc[qb][4 * rr + 1] * a.scale);
+        v2[1] = pack2<T>(dkacc[qb][4 * rr + 2] * a.scale, dkacc[qb][4 * rr + 3] * a.scale);
+        *(u32x2*)(dkr + d) = v2;
+      }
+    }
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int d = 32 * vb + 8 * rr + 4 * g;
+        u32x2 v2;
+        v2[0] = pack2<T>(dvacc[vb][4 * rr] * rescale, dvacc[vb][4 * rr + 1] * rescale);
+        v2[1] = pack2<T>(dvacc[vb][4 * rr + 2] * rescale, dvacc[vb][4 * rr + 3] * rescale);
+        *(u32x2*)(dvr + d) = v2;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Workgroup = 4 waves x 32 query rows; key tiles of 64.  Each wave keeps
+// Q^T and dO^T of its rows in registers and, per key tile, forms
+//   S^T = K Q^T,  dP^T = V dO^T   (A operands: K, V rows from LDS)
+//   dS^T = P^T o (dP^T - D)       (one query row per lane)
+//   dQ^T += K^T dS^T              (A = K^T via the transposing LDS read)
+template <int DQK, int DV, bool DROP> struct DqOcc {
+  static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
+};
+
+template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(const BwdArgs a) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32;
+  __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int sq = sp.sq, skv = sp.skv;
+  const int q0 = mt * BR;
+  if (q0 >= sq) return;
+
+  const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
+  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
+  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
+  const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
+  const uint16_t* bg = nullptr;
+  if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+
+  const int kv_end = CAUSAL ? min(skv, q0 + BR) : skv;
+  const int nt = (kv_end + BC - 1) / BC;
+  const int row = q0 + 32 * w + l32;
+  const bool row_ok = row < sq;
+
+  u32x4 qreg[KT], doreg[VT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    qreg[t] = row_ok ? *(const u32x4*)(qg + (int64_t)row * a.sq_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < VT; ++t)
+    doreg[t] = row_ok ? *(const u32x4*)(dog + (int64_t)row * a.sdo_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+  float lse2 = 0.f, Drow = 0.f;
+  if (row_ok) {
+    lse2 = a.lse[row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0) + row] * kLog2e;
+    Drow = a.dvec[row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + row];
+  }
+
+  DropKey dk{};
+  const uint32_t bh = (uint32_t)(b * a.H + h);
+  if (DROP) dk = drop_key(a.drop);
+  const float rescale = DROP ? a.drop.rescale : 1.f;
+
+  f32x16 dqacc[QB];
+#pragma unroll
+  for (int i = 0; i < QB; ++i) dqacc[i] = f32x16{};
+
+  if (nt > 0) {
+    tile_load_direct<DQK, BC>(sK[0], kg, a.sk_.s, 0, skv, w, lane);
+    tile_load_direct<DV, BC>(sV[0], vg, a.sv_.s, 0, skv, w, lane);
+  }
+  for (int it = 0; it < nt; ++it) {
+    const int n0 = it * BC;
+    const T* cK = sK[it & 1];
+    const T* cV = sV[it & 1];
+    wait_all();
+    __syncthreads();
+    const bool active = !CAUSAL || (n0 <= q0 + 32 * w + 31);
+
+    uint32_t braw[4][4];
+    if (BIAS && active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int kb = n0 + 16 * u + 8 * g;
+        const uint16_t* p = bg + (int64_t)row * a.sb_.s + kb;
+        if (row_ok && kb + 8 <= skv && a.bias_vec) {
+          u32x4 x = *(const u32x4*)p;
+          braw[u][0] = x[0]; braw[u][1] = x[1]; braw[u][2] = x[2]; braw[u][3] = x[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t lo = (row_ok && kb + 2 * e < skv) ? p[2 * e] : 0;
+            uint32_t hi = (row_ok && kb + 2 * e + 1 < skv) ? p[2 * e + 1] : 0;
+            braw[u][e] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+
+    if (it + 1 < nt) {
+      tile_load_direct<DQK, BC>(sK[(it + 1) & 1], kg, a.sk_.s, n0 + BC, skv, w, lane);
+      tile_load_direct<DV, BC>(sV[(it + 1) & 1], vg, a.sv_.s, n0 + BC, skv, w, lane);
+    }
+    if (!active) continue;
+
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 a0 = lds_rowA<DQK>(cK, 0, 16 * t, lane);
+      u32x4 a1 = lds_rowA<DQK>(cK, 32, 16 * t, lane);
+      s[0] = mfma32<T>(a0, qreg[t], s[0]);
+      s[1] = mfma32<T>(a1, qreg[t], s[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      u32x4 a0 = lds_rowA<DV>(cV, 0, 16 * t, lane);
+      u32x4 a1 = lds_rowA<DV>(cV, 32, 16 * t, lane);
+      dp[0] = mfma32<T>(a0, doreg[t], dp[0]);
+      dp[1] = mfma32<T>(a1, doreg[t], dp[1]);
+    }
+
+    uint32_t kw[8];
+    if (DROP) {
+      uint32_t var4[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((n0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
+      quad_keep_words<true>(var4, (uint32_t)row >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
+    }
+
+    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
+    u32x4 dsb[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[blk][r] * a.scale_log2 - lse2;
+        if (BIAS) {
+          int u = 2 * blk + (r >> 3), e = r & 7;
+          uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          x += to_f32<T>((uint16_t)bits) * kLog2e;
+        }
+        float p = __builtin_amdgcn_exp2f(x);
+        if (need_mask || !row_ok) {
+          int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+          bool vis = row_ok && kv < skv && (!CAUSAL || kv <= row);
+          p = vis ? p : 0.f;
+        }
+        float z = 1.f;
+        if (DROP) {
+          int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
+          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          z = keep ? rescale : 0.f;
+        }
+        s[blk][r] = p * (dp[blk][r] * z - Drow);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      int blk = tt >> 1, r0 = 8 * (tt & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 ak = lds_trA<DQK>(cK, 16 * tt, 32 * qb, lane);
+        dqacc[qb] = mfma32<T>(ak, dsb[tt], dqacc[qb]);
+      }
+    }
+  }
+
+  if (row_ok) {
+    T* dqr = base_ptr_mut<T>(a.dq, a.sdq_, sp, h, true) + (int64_t)row * a.sdq_.s;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int d = 32 * qb + 8 * rr + 4 * g;
+        u32x2 v2;
+        v2[0] = pack2<T>(dqacc[qb][4 * rr] * a.scale, dqacc[qb][4 * rr + 1] * a.scale);
+        v2[1] = pack2<T>(dqacc[qb][4 * rr + 2] * a.scale, dqacc[qb][4 * rr + 3] * a.scale);
+        *(u32x2*)(dqr + d) = v2;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 io: one wavefront per query row (dQ) or per key (dK, dV, dBias).
+template <bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int i = blockIdx.x * 4 + w;
+  if (i >= sp.sq) return;
+  const float* qi = base_ptr<float>(a.q, a.sq_, sp, h, true) + (int64_t)i * a.sq_.s;
+  const float* doi = base_ptr<float>(a.dout, a.sdo_, sp, h, true) + (int64_t)i * a.sdo_.s;
+  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h, false);
+  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h, false);
+  const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
+                                 (int64_t)i * a.sb_.s
+                           : nullptr;
+  DropKey dk{};
+  if (DROP) dk = drop_key(a.drop);
+  const uint32_t bh = (uint32_t)(b * a.H + h);
+  const float lse = a.lse[row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0) + i];
+  const float Di = a.dvec[row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + i];
+  float q[4], dO[4], acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    q[c] = d < dqk ? qi[d] : 0.f;
+    dO[c] = d < dv ? doi[d] : 0.f;
+    acc[c] = 0.f;
+  }
+  int last = sp.skv - 1;
+  if (CAUSAL && i < last) last = i;
+  for (int j = 0; j <= last; ++j) {
+    const float* kj = kg + (int64_t)j * a.sk_.s;
+    const float* vj = vg + (int64_t)j * a.sv_.s;
+    float ps = 0.f, pd = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      if (d < dqk) ps += q[c] * kj[d];
+      if (d < dv) pd += dO[c] * vj[d];
+    }
+    float s = wave_sum(ps) * a.scale + (BIAS ? brow[j] : 0.f);
+    float dp = wave_sum(pd);
+    float p = expf(s - lse);
+    float z = 1.f;
+    if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
+    float ds = p * (dp * z - Di);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      if (d < dqk) acc[c] += ds * kj[d];
+    }
+  }
+  float* dqi = base_ptr_mut<float>(a.dq, a.sdq_, sp, h, true) + (int64_t)i * a.sdq_.s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    if (d < dqk) dqi[d] = acc[c] * a.scale;
+  }
+}
+
+template <bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int j = blockIdx.x * 4 + w;
+  if (j >= sp.skv) return;
+  const float* kj = base_ptr<float>(a.k, a.sk_, sp, h, false) + (int64_t)j * a.sk_.s;
+  const float* vj = base_ptr<float>(a.v, a.sv_, sp, h, false) + (int64_t)j * a.sv_.s;
+  const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true);
+  const float* dog = base_ptr<float>(a.dout, a.sdo_, sp, h, true);
+  const float* bcol = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h + j : nullptr;
+  float* dbcol = (BIAS && a.dbias) ? (float*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h + j
+                                   : nullptr;
+  DropKey dk{};
+  if (DROP) dk = drop_key(a.drop);
+  const uint32_t bh = (uint32_t)(b * a.H + h);
+  const int64_t lse_base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+  const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+  float k[4], v[4], gk[4], gv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    k[c] = d < dqk ? kj[d] : 0.f;
+    v[c] = d < dv ? vj[d] : 0.f;
+    gk[c] = 0.f;
+    gv[c] = 0.f;
+  }
+  const int i0 = CAUSAL ? min(j, sp.sq) : 0;
+  if (dbcol && lane == 0)
+    for (int i = 0; i < i0; ++i) dbcol[(int64_t)i * a.sdb_.s] = 0.f;
+  for (int i = i0; i < sp.sq; ++i) {
+    const float* qi = qg + (int64_t)i * a.sq_.s;
+    const float* doi = dog + (int64_t)i * a.sdo_.s;
+    float ps = 0.f, pd = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      if (d < dqk) ps += qi[d] * k[c];
+      if (d < dv) pd += doi[d] * v[c];
+    }
+    float s = wave_sum(ps) * a.scale + (BIAS ? bcol[(int64_t)i * a.sb_.s] : 0.f);
+    float dp = wave_sum(pd);
+    float p = expf(s - a.lse[lse_base + i]);
+    float z = 1.f;
+    if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
+    float ds = p * (dp * z - a.dvec[d_base + i]);
+    if (dbcol && lane == 0) dbcol[(int64_t)i * a.sdb_.s] = ds;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      if (d < dqk) gk[c] += ds * qi[d];
+      if (d < dv) gv[c] += p * z * doi[d];
+    }
+  }
+  float* dkj = base_ptr_mut<float>(a.dk, a.sdk_, sp, h, false) + (int64_t)j * a.sdk_.s;
+  float* dvj = base_ptr_mut<float>(a.dv, a.sdv_, sp, h, false) + (int64_t)j * a.sdv_.s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    if (d < dqk) dkj[d] = gk[c] * a.scale;
+    if (d < dv) dvj[d] = gv[c];
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
+  dim3 grid((a.seq.s_q + 15) / 16, a.H, a.B), block(256);
+  if (t == IoType::BF16) hipLaunchKernelGGL(bwd_pre<__bf16>, grid, block, 0, st, a, dv);
+  else if (t == IoType::F16) hipLaunchKernelGGL(bwd_pre<_Float16>, grid, block, 0, st, a, dv);
+  else hipLaunchKernelGGL(bwd_pre<float>, grid, block, 0, st, a, dv);
+  return hipGetLastError();
+}
+
+#define SDPA_FLAG_SWITCH(LAUNCH)              \
+  if (!causal && !bias && !drop) LAUNCH(false, false, false) \
+  if (causal && !bias && !drop) LAUNCH(true, false, false)   \
+  if (!causal && bias && !drop) LAUNCH(false, true, false)   \
+  if (causal && bias && !drop) LAUNCH(true, true, false)     \
+  if (!causal && !bias && drop) LAUNCH(false, false, true)   \
+  if (causal && !bias && drop) LAUNCH(true, false, true)     \
+  if (!causal && bias && drop) LAUNCH(false, true, true)     \
+  if (causal && bias && drop) LAUNCH(true, true, true)
+
+template <typename T, int DQK, int DV>
+static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
+  dim3 grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(256);
+#define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
+  SDPA_FLAG_SWITCH(L)
+#undef L
+  return hipErrorInvalidValue;
+}
+template <typename T, int DQK, int DV>
+static hipError_t dq_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
+  dim3 grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
+#define L(C, BI, DR) { hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
+  SDPA_FLAG_SWITCH(L)
+#undef L
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t dkdv_type(int dqk, int dv, bool causal, bool bias, bool drop, const BwdArgs& a,
+                            hipStream_t st) {
+  if (dqk == 64 && dv == 64) return dkdv_dims<T, 64, 64>(causal, bias, drop, a, st);
+  if (dqk == 128 && dv == 128) return dkdv_dims<T, 128, 128>(causal, bias, drop, a, st);
+  if (dqk == 192 && dv == 128) return dkdv_dims<T, 192, 128>(causal, bias, drop, a, st);
+  return hipErrorInvalidValue;
+}
+template <typename T>
+static hipError_t dq_type(int dqk, int dv, bool causal, bool bias, bool drop, const BwdArgs& a,
+                          hipStream_t st) {
+  if (dqk == 64 && dv == 64) return dq_dims<T, 64, 64>(causal, bias, drop, a, st);
+  if (dqk == 128 && dv == 128) return dq_dims<T, 128, 128>(causal, bias, drop, a, st);
+  if (dqk == 192 && dv == 128) return dq_dims<T, 192, 128>(causal, bias, drop, a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st) {
+  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  if (t == IoType::BF16) return dkdv_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
+  if (t == IoType::F16) return dkdv_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
+  dim3 grid((a.seq.s_kv + 3) / 4, a.H, a.B), block(256);
+#define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
+  SDPA_FLAG_SWITCH(L)
+#undef L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st) {
+  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  if (t == IoType::BF16) return dq_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
+  if (t == IoType::F16) return dq_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
+  dim3 grid((a.seq.s_q + 3) / 4, a.H, a.B), block(256);
+#define L(C, BI, DR) { hipLaunchKernelGGL((dq_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
+  SDPA_FLAG_SWITCH(L)
+#undef L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,358 @@
+// Forward attention kernels for gfx950.
+//
+// What is computed (Composable Kernel "fmha_bwd_kernel.hpp Source File",
+// formula comment S, S', S'', P; PyTorch "MHA.cpp" run_cudnn_SDP_fprop for
+// the O and fp32 stats outputs): O = softmax(scale * Q K^T + Bias, masked)
+// (dropped out) V, and LSE = row log-sum-exp (natural log).
+//
+// MFMA kernel (16-bit io).  One workgroup = 4 wavefronts = 128 query rows of
+// one (batch, head) - the query-stationary grid of oneDNN's execute_forward
+// (q tiles x heads x batch).  Each wave keeps its 32 query rows of Q in
+// registers as the B operand and computes the transposed score tile
+// S^T = K Q^T (keys x queries) per 64-key tile, so a lane owns one query
+// row: the row max and row sum are lane-local apart from one exchange with
+// lane l^32.  With the keys fetched in sig-permuted order, the probabilities
+// come out of the accumulators already in the B-operand layout of the second
+// product O^T += V^T P^T, whose A operand is read from the natural [key][d]
+// V tile in LDS with the gfx950 transposing LDS read.  Softmax runs in base
+// 2 with log2(e) folded into the scale (CK stores scale*log2e beside the raw
+// scale in its kernel arguments).
+#include "sdpa_kcommon.h"
+
+namespace sdpa {
+
+// workgroups per CU the register budget is sized for
+template <int DQK, int DV, bool DROP> struct FwdOcc {
+  static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
+};
+
+template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(const FwdArgs a) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
+  constexpr int DB = DV / 32;   // 32-wide blocks of d_v
+  __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];  // double-buffered tiles
+  __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;  // heavy first
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int sq = sp.sq, skv = sp.skv;
+  const int q0 = mt * BR;
+  if (q0 >= sq) return;
+
+  const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
+  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
+  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
+  T* og = base_ptr_mut<T>(a.o, a.so_, sp, h, true);
+  const uint16_t* bg = nullptr;
+  if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+
+  const int kv_end = CAUSAL ? min(skv, q0 + BR) : skv;
+  const int nt = (kv_end + BC - 1) / BC;
+
+  const int row = q0 + 32 * w + l32;  // this lane's query row
+  const bool row_ok = row < sq;
+  u32x4 qreg[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    qreg[t] = row_ok ? *(const u32x4*)(qg + (int64_t)row * a.sq_.s + 16 * t + 8 * g)
+                     : u32x4{0, 0, 0, 0};
+
+  DropKey dk{};
+  uint32_t bh = (uint32_t)(b * a.H + h);
+  if (DROP) dk = drop_key(a.drop);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (nt > 0) {
+    tile_load_direct<DQK, BC>(sK[0], kg, a.sk_.s, 0, skv, w, lane);
+    tile_load_direct<DV, BC>(sV[0], vg, a.sv_.s, 0, skv, w, lane);
+  }
+  for (int it = 0; it < nt; ++it) {
+    const int n0 = it * BC;
+    const T* cK = sK[it & 1];
+    const T* cV = sV[it & 1];
+    wait_all();       // this wave's part of tile `it` has landed
+    __syncthreads();  // ... and everyone's; tile it-1 is fully consumed
+
+    // a wave whose rows see none of this tile skips it (causal)
+    const bool active = !CAUSAL || (n0 <= q0 + 32 * w + 31);
+
+    // bias for this lane's row: 4 runs of 8 consecutive keys (issued before
+    // the next tile's prefetch so that waiting for them does not wait for it)
+    uint32_t braw[4][4];
+    if (BIAS && active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int kb = n0 + 16 * u + 8 * g;  // u = 2*blk + hh
+        const uint16_t* p = bg + (int64_t)row * a.sb_.s + kb;
+        if (row_ok && kb + 8 <= skv && a.bias_vec) {
+          u32x4 x = *(const u32x4*)p;
+          braw[u][0] = x[0]; braw[u][1] = x[1]; braw[u][2] = x[2]; braw[u][3] = x[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t lo = (row_ok && kb + 2 * e < skv) ? p[2 * e] : 0;
+            uint32_t hi = (row_ok && kb + 2 * e + 1 < skv) ? p[2 * e + 1] : 0;
+            braw[u][e] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+    if (it + 1 < nt) {
+      tile_load_direct<DQK, BC>(sK[(it + 1) & 1], kg, a.sk_.s, n0 + BC, skv, w, lane);
+      tile_load_direct<DV, BC>(sV[(it + 1) & 1], vg, a.sv_.s, n0 + BC, skv, w, lane);
+    }
+    if (!active) continue;
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 a0 = lds_rowA<DQK>(cK, 0, 16 * t, lane);
+      u32x4 a1 = lds_rowA<DQK>(cK, 32, 16 * t, lane);
+      s[0] = mfma32<T>(a0, qreg[t], s[0]);
+      s[1] = mfma32<T>(a1, qreg[t], s[1]);
+    }
+
+    // keep bytes (dropout): 8 runs of 4 keys
+    uint32_t kw[8];
+    if (DROP) {
+      uint32_t var4[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((n0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
+      quad_keep_words<true>(var4, (uint32_t)row >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
+    }
+
+    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[blk][r] * a.scale_log2;
+        if (BIAS) {
+          int u = 2 * blk + (r >> 3), e = r & 7;
+          uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          x += to_f32<T>((uint16_t)bits) * kLog2e;
+        }
+        if (need_mask) {
+          int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+          bool vis = kv < skv && (!CAUSAL || kv <= row);
+          x = vis ? x : -INFINITY;
+        }
+        s[blk][r] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    }
+    const float m_new = fmaxf(m_run, max_pair32(mloc));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+    u32x4 pb[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(s[blk][r] - m_use);
+        psum += pv;
+        if (DROP) {
+          int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
+          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          pv = keep ? pv : 0.f;
+        }
+        s[blk][r] = pv;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      int blk = tt >> 1, r0 = 8 * (tt & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+
+    if (DROP && a.keep && row_ok) {
+      uint8_t* kp = a.keep + (((int64_t)b * a.H + h) * a.seq.s_q + row) * a.seq.s_kv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        int kv0 = n0 + 16 * (k >> 1) + 8 * g + 4 * (k & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int kv = kv0 + e;
+          if (kv < skv && (!CAUSAL || kv <= row))
+            kp[kv] = ((kw[k] >> (8 * e)) & 0xffu) >= dk.thr ? 1 : 0;
+        }
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 av = lds_trA<DV>(cV, 16 * tt, 32 * db, lane);
+        oacc[db] = mfma32<T>(av, pb[tt], oacc[db]);
+      }
+    }
+  }
+
+  // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2
+  const float l_row = sum_pair32(l_run);
+  float fac = l_row > 0.f ? 1.f / l_row : 0.f;
+  if (DROP) fac *= a.drop.rescale;
+  if (row_ok) {
+    T* orow = og + (int64_t)row * a.so_.s;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int d = 32 * db + 8 * rr + 4 * g;
+        u32x2 v2;
+        v2[0] = pack2<T>(oacc[db][4 * rr + 0] * fac, oacc[db][4 * rr + 1] * fac);
+        v2[1] = pack2<T>(oacc[db][4 * rr + 2] * fac, oacc[db][4 * rr + 3] * fac);
+        *(u32x2*)(orow + d) = v2;
+      }
+    }
+    if (a.lse && g == 0) {
+      int64_t base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      a.lse[base + row] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// fp32 io: one wavefront per query row, the head dims spread over lanes.
+template <bool CAUSAL, bool BIAS, bool DROP>
+__global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int row = blockIdx.x * 4 + w;
+  if (row >= sp.sq) return;
+  const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true) + (int64_t)row * a.sq_.s;
+  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h, false);
+  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h, false);
+  float* og = base_ptr_mut<float>(a.o, a.so_, sp, h, true) + (int64_t)row * a.so_.s;
+  const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
+                                 (int64_t)row * a.sb_.s
+                           : nullptr;
+  DropKey dk{};
+  if (DROP) dk = drop_key(a.drop);
+  const uint32_t bh = (uint32_t)(b * a.H + h);
+  float q[4], o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    q[c] = d < dqk ? qg[d] : 0.f;
+    o[c] = 0.f;
+  }
+  int last = sp.skv - 1;
+  if (CAUSAL && row < last) last = row;
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= last; ++j) {
+    const float* kj = kg + (int64_t)j * a.sk_.s;
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      if (d < dqk) part += q[c] * kj[d];
+    }
+    float sc = wave_sum(part) * a.scale + (BIAS ? brow[j] : 0.f);
+    float mn = fmaxf(m, sc);
+    float alpha = expf(m - mn);
+    float p = expf(sc - mn);
+    l = l * alpha + p;
+    m = mn;
+    float pz = p;
+    if (DROP) {
+      bool keep = keep_one(dk, bh, row, j);
+      pz = keep ? p : 0.f;
+      if (a.keep && lane == 0)
+        a.keep[(((int64_t)b * a.H + h) * a.seq.s_q + row) * a.seq.s_kv + j] = keep ? 1 : 0;
+    }
+    const float* vj = vg + (int64_t)j * a.sv_.s;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d = lane + 64 * c;
+      o[c] = o[c] * alpha + (d < dv ? pz * vj[d] : 0.f);
+    }
+  }
+  float fac = l > 0.f ? 1.f / l : 0.f;
+  if (DROP) fac *= a.drop.rescale;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    int d = lane + 64 * c;
+    if (d < dv) og[d] = o[c] * fac;
+  }
+  if (a.lse && lane == 0) {
+    int64_t base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+    a.lse[base + row] = l > 0.f ? m + logf(l) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV>
+static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const FwdArgs& a,
+                                     hipStream_t st) {
+  dim3 grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
+#define SDPA_FWD_CASE(C, BI, DR)                                                 \
+  if (causal == C && bias == BI && drop == DR) {                                 \
+    hipLaunchKernelGGL((fwd_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); \
+    return hipGetLastError();                                                    \
+  }
+  SDPA_FWD_CASE(false, false, false)
+  SDPA_FWD_CASE(true, false, false)
+  SDPA_FWD_CASE(false, true, false)
+  SDPA_FWD_CASE(true, true, false)
+  SDPA_FWD_CASE(false, false, true)
+  SDPA_FWD_CASE(true, false, true)
+  SDPA_FWD_CASE(false, true, true)
+  SDPA_FWD_CASE(true, true, true)
+#undef SDPA_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t fwd_dispatch_dims(int dqk, int dv, bool causal, bool bias, bool drop,
+                                    const FwdArgs& a, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return fwd_dispatch_flags<T, 64, 64>(causal, bias, drop, a, st);
+  if (dqk == 128 && dv == 128) return fwd_dispatch_flags<T, 128, 128>(causal, bias, drop, a, st);
+  if (dqk == 192 && dv == 128) return fwd_dispatch_flags<T, 192, 128>(causal, bias, drop, a, st);
+  return hipErrorInvalidValue;
+}
+
+bool mfma_dims_supported(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+}
+
+hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a, hipStream_t st) {
+  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  if (t == IoType::BF16) return fwd_dispatch_dims<__bf16>(dqk, dv, causal, bias, drop, a, st);
+  if (t == IoType::F16) return fwd_dispatch_dims<_Float16>(dqk, dv, causal, bias, drop, a, st);
+  dim3 grid((a.seq.s_q + 3) / 4, a.H, a.B), block(256);
+#define SDPA_F32_CASE(C, BI, DR)                                                       \
+  if (causal == C && bias == BI && drop == DR) {                                       \
+    hipLaunchKernelGGL((fwd_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv);           \
+    return hipGetLastError();                                                          \
+  }
+  SDPA_F32_CASE(false, false, false)
+  SDPA_F32_CASE(true, false, false)
+  SDPA_F32_CASE(false, true, false)
+  SDPA_F32_CASE(true, true, false)
+  SDPA_F32_CASE(false, false, true)
+  SDPA_F32_CASE(true, false, true)
+  SDPA_F32_CASE(false, true, true)
+  SDPA_F32_CASE(true, true, true)
+#undef SDPA_F32_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

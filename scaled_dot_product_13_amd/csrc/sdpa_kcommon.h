@@ -1,0 +1,100 @@
+// Per-workgroup problem resolution shared by the attention kernels:
+// sequence extents (batch or group mode), tensor base pointers, the dropout
+// key, and small wave-level helpers for the fp32 path.
+#pragma once
+#include "sdpa_device.h"
+#include "sdpa_params.h"
+
+namespace sdpa {
+
+struct SeqPos {
+  int64_t qtok, ktok;  // first token of this sequence (0 in batch mode)
+  int32_t sq, skv;     // this sequence's lengths
+  int64_t bsel;        // batch index to multiply batch strides by (0 in group mode)
+};
+
+__device__ __forceinline__ SeqPos resolve_seq(const SeqInfo& s, int b) {
+  SeqPos p;
+  if (s.cu_q) {
+    p.qtok = s.cu_q[b];
+    p.sq = s.cu_q[b + 1] - (int32_t)p.qtok;
+    p.ktok = s.cu_kv[b];
+    p.skv = s.cu_kv[b + 1] - (int32_t)p.ktok;
+    p.bsel = 0;
+  } else {
+    p.qtok = 0; p.ktok = 0;
+    p.sq = s.s_q; p.skv = s.s_kv;
+    p.bsel = b;
+  }
+  return p;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* base_ptr(const void* p, const Str& s, const SeqPos& sp,
+                                             int h, bool is_q) {
+  return (const T*)p + sp.bsel * s.b + (int64_t)h * s.h + (is_q ? sp.qtok : sp.ktok) * s.s;
+}
+template <typename T>
+__device__ __forceinline__ T* base_ptr_mut(void* p, const Str& s, const SeqPos& sp, int h,
+                                           bool is_q) {
+  return (T*)p + sp.bsel * s.b + (int64_t)h * s.h + (is_q ? sp.qtok : sp.ktok) * s.s;
+}
+
+// Index of row 0 of (b, h) in a dense per-row fp32 array:
+//   batch mode [B,H,S_q]; group mode [H, T] with T = `group_rows`.
+__device__ __forceinline__ int64_t row_stat_base(const SeqInfo& s, const SeqPos& sp, int b,
+                                                 int h, int H, int64_t group_rows) {
+  if (s.cu_q) return (int64_t)h * group_rows + sp.qtok;
+  return ((int64_t)b * H + h) * s.s_q;
+}
+
+struct DropKey {
+  uint32_t k0, k1, off, thr;
+};
+__device__ __forceinline__ DropKey drop_key(const DropoutArgs& d) {
+  uint64_t seed = d.seed, off = d.offset;
+  if (d.seed_offset_dev) {
+    seed = d.seed_offset_dev[0];
+    off = d.seed_offset_dev[1];
+  }
+  DropKey k;
+  k.k0 = (uint32_t)seed;
+  k.k1 = (uint32_t)(seed >> 32);
+  k.off = (uint32_t)off;
+  k.thr = d.threshold;
+  return k;
+}
+
+// Keep bit of one element from one Philox call (fp32 path, no sharing).
+__device__ __forceinline__ bool keep_one(const DropKey& k, uint32_t bh, int i, int j) {
+  uint32_t r[4];
+  Philox::block((uint32_t)j >> 2, (uint32_t)i >> 2, bh, k.off, k.k0, k.k1, r);
+  uint32_t w = r[i & 3];
+  return ((w >> (8 * (j & 3))) & 0xffu) >= k.thr;
+}
+
+// Wave-wide sum with every lane receiving lane 0's value (bitwise uniform).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return __shfl(x, 0, 64);
+}
+
+template <typename T> __device__ __forceinline__ float ld_elem(const T* p);
+template <> __device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld_elem<__bf16>(const __bf16* p) {
+  return to_f32<__bf16>(*(const uint16_t*)p);
+}
+template <> __device__ __forceinline__ float ld_elem<_Float16>(const _Float16* p) {
+  return to_f32<_Float16>(*(const uint16_t*)p);
+}
+template <typename T> __device__ __forceinline__ void st_elem(T* p, float v);
+template <> __device__ __forceinline__ void st_elem<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st_elem<__bf16>(__bf16* p, float v) {
+  *(uint16_t*)p = (uint16_t)(pack2<__bf16>(v, 0.f) & 0xffffu);
+}
+template <> __device__ __forceinline__ void st_elem<_Float16>(_Float16* p, float v) {
+  *(uint16_t*)p = (uint16_t)(pack2<_Float16>(v, 0.f) & 0xffffu);
+}
+
+}  // namespace sdpa

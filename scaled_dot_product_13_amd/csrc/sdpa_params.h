@@ -1,0 +1,72 @@
+// Kernel argument blocks and launcher declarations shared by the host API
+// (sdpa_api.cpp) and the kernels (sdpa_*.hip).  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+enum class IoType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Strides in elements; the innermost dimension is contiguous.
+struct Str {
+  int64_t b, h, s;
+};
+
+// Where the sequences of one batch entry live.  In batch mode every entry
+// has s_q / s_kv rows starting at row 0 of its (b, h) slice; in group mode
+// the rows of sequence b start at token cu_q[b] (cu_kv[b]) of a packed
+// tensor and the batch stride is unused.
+struct SeqInfo {
+  const int32_t* cu_q;   // null in batch mode
+  const int32_t* cu_kv;
+  int32_t s_q, s_kv;     // batch mode lengths (group mode: maxima, grid sizing only)
+};
+
+struct DropoutArgs {
+  int32_t enabled;                  // p > 0
+  uint32_t threshold;               // keep iff random byte >= threshold
+  float rescale;                    // 1 / (1 - p)
+  uint64_t seed, offset;            // used when seed_offset_dev is null
+  const uint64_t* seed_offset_dev;  // optional device {seed, offset}
+};
+
+struct FwdArgs {
+  const void *q, *k, *v, *bias;
+  void* o;
+  float* lse;       // nullable
+  uint8_t* keep;    // nullable, dense [B,H,S_q,S_kv], batch mode only
+  Str sq_, sk_, sv_, sb_, so_;
+  int32_t bias_vec;  // bias rows 16-byte aligned: vector loads allowed
+  int32_t B, H;
+  SeqInfo seq;
+  float scale;         // scaling_factor
+  float scale_log2;    // scaling_factor * log2(e)
+  DropoutArgs drop;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *bias, *o, *dout;
+  const float* lse;
+  float* dvec;      // D workspace: batch [B,H,S_q]; group [H, B*S_q]
+  void *dq, *dk, *dv, *dbias;
+  Str sq_, sk_, sv_, sb_, so_, sdo_, sdq_, sdk_, sdv_, sdb_;
+  int32_t bias_vec;
+  int32_t B, H;
+  SeqInfo seq;
+  float scale, scale_log2;
+  DropoutArgs drop;
+};
+
+// Launchers (each returns hipSuccess or the launch error).  `causal`,
+// `bias` and `dropout` select template instances.
+hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a,
+                      hipStream_t st);
+hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs& a,
+                           hipStream_t st);
+hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a,
+                         hipStream_t st);
+bool mfma_dims_supported(int dqk, int dv);
+
+}  // namespace sdpa

@@ -1,0 +1,222 @@
+"""Thin ctypes binding of libsdpa.so (include/sdpa.h), same entry-point names.
+
+Argument marshalling only: torch tensors supply device memory, strides and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if libsdpa.so is missing this module
+raises on import.
+
+Output allocation follows PyTorch's cuDNN attention glue ("MHA.cpp",
+alloc_with_matching_layout): outputs take the stride order of the
+corresponding input; dO is made unit-stride in its last dimension
+(permute_to_matching_layout / the bprop stride fix).
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} not found: build it first (python -m scaled_dot_product_13_amd.build "
+        "or __graft_entry__.build()); there is no fallback implementation")
+
+SDPA_OK, SDPA_ERR_INVALID_ARG, SDPA_ERR_UNSUPPORTED, SDPA_ERR_WORKSPACE, SDPA_ERR_HIP = range(5)
+SDPA_F32, SDPA_F16, SDPA_BF16 = 0, 1, 2
+_DTYPES = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: SDPA_BF16}
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("seq", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("dtype", ctypes.c_int),
+        ("b", ctypes.c_int64), ("h", ctypes.c_int64),
+        ("s_q", ctypes.c_int64), ("s_kv", ctypes.c_int64),
+        ("d_qk", ctypes.c_int64), ("d_v", ctypes.c_int64),
+        ("scaling_factor", ctypes.c_float), ("is_causal", ctypes.c_int32),
+        ("dropout_probability", ctypes.c_float),
+        ("dropout_seed", ctypes.c_uint64), ("dropout_offset", ctypes.c_uint64),
+        ("dropout_seed_offset_dev", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
+    ]
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+_P = ctypes.POINTER(Problem)
+_lib.sdpa_fwd_workspace_size.argtypes = [_P]
+_lib.sdpa_fwd_workspace_size.restype = _sz
+_lib.sdpa_bwd_workspace_size.argtypes = [_P]
+_lib.sdpa_bwd_workspace_size.restype = _sz
+_lib.sdpa_fwd.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                          _vp, Strides, _vp, _vp, _vp, _sz, _vp]
+_lib.sdpa_fwd.restype = ctypes.c_int
+_lib.sdpa_bwd.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                          _vp, Strides, _vp, Strides, _vp, _vp, Strides, _vp, Strides,
+                          _vp, Strides, _vp, Strides, _vp, _sz, _vp]
+_lib.sdpa_bwd.restype = ctypes.c_int
+_lib.sdpa_bwd_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, _vp]
+_lib.sdpa_bwd_preprocess.restype = ctypes.c_int
+_lib.sdpa_status_string.argtypes = [ctypes.c_int]
+_lib.sdpa_status_string.restype = ctypes.c_char_p
+_lib.sdpa_last_error_message.restype = ctypes.c_char_p
+_lib.sdpa_version.restype = ctypes.c_char_p
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_lib.sdpa_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != SDPA_OK:
+        raise SdpaError(status, _lib.sdpa_last_error_message().decode())
+
+
+def version() -> str:
+    return _lib.sdpa_version().decode()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t, group):
+    if t is None:
+        return Strides(0, 0, 0)
+    s = t.stride()
+    if group:  # [T, H, D]
+        return Strides(0, s[1], s[0])
+    return Strides(s[0], s[1], s[2])
+
+
+def _alloc_like(ref, shape, dtype=None):
+    """Allocate `shape` with the stride order of `ref` (same rank)."""
+    order = sorted(range(ref.dim()), key=lambda i: -ref.stride(i))
+    perm_shape = [shape[i] for i in order]
+    out = torch.empty(perm_shape, dtype=dtype or ref.dtype, device=ref.device)
+    inv = [0] * len(order)
+    for pos, i in enumerate(order):
+        inv[i] = pos
+    return out.permute(inv)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
+                 seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
+                 max_seqlen_kv=None):
+    """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group [T,H,D])."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    group = cu_seqlens_q is not None
+    p = Problem()
+    p.struct_size = ctypes.sizeof(Problem)
+    p.dtype = _DTYPES[q.dtype]
+    if group:
+        p.b = cu_seqlens_q.numel() - 1
+        p.h = q.shape[1]
+        p.s_q = int(max_seqlen_q)
+        p.s_kv = int(max_seqlen_kv)
+        p.d_qk, p.d_v = q.shape[2], v.shape[2]
+        p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        p.cu_seqlens_kv = cu_seqlens_kv.data_ptr()
+    else:
+        p.b, p.h, p.s_q, p.d_qk = q.shape
+        p.s_kv, p.d_v = k.shape[2], v.shape[3]
+    p.scaling_factor = float(scale if scale is not None else 1.0 / math.sqrt(p.d_qk))
+    p.is_causal = 1 if causal else 0
+    p.dropout_probability = float(dropout_p)
+    p.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    p.dropout_offset = int(offset) & 0xFFFFFFFFFFFFFFFF
+    p.dropout_seed_offset_dev = seed_offset.data_ptr() if seed_offset is not None else None
+    return p
+
+
+def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
+             seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
+             max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None):
+    """Forward.  Returns (o, lse or None, keep or None)."""
+    group = cu_seqlens_q is not None
+    p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
+                     offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
+                     cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
+                     max_seqlen_kv=max_seqlen_kv)
+    if out is None:
+        oshape = list(q.shape)
+        oshape[-1] = v.shape[-1]
+        out = _alloc_like(q, oshape)
+    if return_lse and lse is None:
+        lse = (torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device) if group
+               else torch.empty((p.b, p.h, p.s_q), dtype=torch.float32, device=q.device))
+    keep = None
+    if return_keep:
+        keep = torch.zeros((p.b, p.h, p.s_q, p.s_kv), dtype=torch.uint8, device=q.device)
+    ws_n = _lib.sdpa_fwd_workspace_size(ctypes.byref(p))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
+    _check(_lib.sdpa_fwd(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
+                         _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
+                         _ptr(out), _strides(out, group), _ptr(lse if return_lse else None),
+                         _ptr(keep), _ptr(ws), ws_n, _stream()))
+    return out, (lse if return_lse else None), keep
+
+
+def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, dropout_p=0.0,
+             seed=0, offset=0, seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+             max_seqlen_q=None, max_seqlen_kv=None, want_dbias=False, workspace=None):
+    """Backward.  Returns (dq, dk, dv, dbias or None)."""
+    group = cu_seqlens_q is not None
+    p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
+                     offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
+                     cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
+                     max_seqlen_kv=max_seqlen_kv)
+    if dout.stride(-1) != 1:
+        dout = dout.contiguous()
+    dq, dk, dv = _alloc_like(q, q.shape), _alloc_like(k, k.shape), _alloc_like(v, v.shape)
+    dbias = _alloc_like(bias, bias.shape) if (want_dbias and bias is not None) else None
+    ws_n = _lib.sdpa_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None or workspace.numel() < ws_n:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.sdpa_bwd(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
+                         _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
+                         _ptr(o), _strides(o, group), _ptr(dout), _strides(dout, group), _ptr(lse),
+                         _ptr(dq), _strides(dq, group), _ptr(dk), _strides(dk, group),
+                         _ptr(dv), _strides(dv, group), _ptr(dbias), _strides(dbias, False),
+                         _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dbias
+
+
+def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, b=None):
+    """D = rowsum(dO o O) in fp32: [B,H,S_q] (group mode [H, B*max_seqlen_q])."""
+    group = cu_seqlens_q is not None
+    p = Problem()
+    p.struct_size = ctypes.sizeof(Problem)
+    p.dtype = _DTYPES[o.dtype]
+    if group:
+        p.b = cu_seqlens_q.numel() - 1
+        p.h, p.d_v = o.shape[1], o.shape[2]
+        p.s_q = p.s_kv = int(max_seqlen_q)
+        p.cu_seqlens_q = p.cu_seqlens_kv = cu_seqlens_q.data_ptr()
+        d = torch.empty((p.h, p.b * p.s_q), dtype=torch.float32, device=o.device)
+    else:
+        p.b, p.h, p.s_q, p.d_v = o.shape
+        p.s_kv = 1
+        d = torch.empty((p.b, p.h, p.s_q), dtype=torch.float32, device=o.device)
+    p.d_qk = p.d_v
+    p.scaling_factor = 1.0
+    _check(_lib.sdpa_bwd_preprocess(ctypes.byref(p), _ptr(o), _strides(o, group), _ptr(dout),
+                                    _strides(dout, group), _ptr(d), _stream()))
+    return d
