@@ -166,6 +166,35 @@ sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t *problem,
                                   const void *d_o, sdpa_strides_t do_strides,
                                   float *d_out, void *stream);
 
+/* The backward's two main kernels, one call each.  sdpa_bwd runs
+ * preprocess -> dK/dV -> dQ on one stream; the dK/dV and dQ kernels read only
+ * the forward's inputs and outputs and D, never each other's results, so a
+ * caller may instead run sdpa_bwd_preprocess and then these two on two
+ * streams, or time them one by one.  `d` is D as written by
+ * sdpa_bwd_preprocess (dense fp32 [b,h,s_q], group mode [h, b*s_q]).
+ * sdpa_bwd_dkdv writes dk, dv and (nullable) dbias; sdpa_bwd_dq writes dq.
+ * Errors as for sdpa_bwd (no workspace involved). */
+sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t *problem,
+                            const void *q, sdpa_strides_t q_strides,
+                            const void *k, sdpa_strides_t k_strides,
+                            const void *v, sdpa_strides_t v_strides,
+                            const void *attn_bias, sdpa_strides_t bias_strides,
+                            const void *d_o, sdpa_strides_t do_strides,
+                            const float *softmax_lse, const float *d,
+                            void *dk, sdpa_strides_t dk_strides,
+                            void *dv, sdpa_strides_t dv_strides,
+                            void *dbias, sdpa_strides_t dbias_strides,
+                            void *stream);
+sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t *problem,
+                          const void *q, sdpa_strides_t q_strides,
+                          const void *k, sdpa_strides_t k_strides,
+                          const void *v, sdpa_strides_t v_strides,
+                          const void *attn_bias, sdpa_strides_t bias_strides,
+                          const void *d_o, sdpa_strides_t do_strides,
+                          const float *softmax_lse, const float *d,
+                          void *dq, sdpa_strides_t dq_strides,
+                          void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sdpa_status_string(sdpa_status_t status);
 

@@ -6,7 +6,8 @@ binding is imported lazily so that `scaled_dot_product_13_amd.build` can run
 before the library exists; touching any API name without a built library
 raises ImportError (there is no fallback path).
 """
-_API = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_preprocess", "make_problem", "SdpaError",
+_API = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_preprocess", "sdpa_bwd_dkdv", "sdpa_bwd_dq",
+        "make_problem", "SdpaError",
         "version", "Problem", "Strides")
 
 

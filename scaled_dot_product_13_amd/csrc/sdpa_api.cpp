@@ -309,4 +309,84 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   return SDPA_OK;
 }
 
+// Shared checks of the operands the dK/dV and dQ kernels read.
+static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
+                                      const void* k, sdpa_strides_t k_s, const void* v,
+                                      sdpa_strides_t v_s, const void* attn_bias,
+                                      sdpa_strides_t bias_s, const void* d_o, sdpa_strides_t do_s,
+                                      const float* lse, const float* d) {
+  sdpa_status_t st;
+  const bool vec = p->dtype != SDPA_F32;
+  if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, v, v_s, "v", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
+  if (!lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null (the backward needs the stats)");
+  if (!d) return fail(SDPA_ERR_INVALID_ARG, "d is null");
+  if (attn_bias) {
+    if (p->cu_seqlens_q) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
+    if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
+  }
+  if (p->d_v % (16 / (int)elem_size(p->dtype)) != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "d_v must fill whole 16-byte chunks");
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
+                            const void* k, sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
+                            const void* attn_bias, sdpa_strides_t bias_s, const void* d_o,
+                            sdpa_strides_t do_s, const float* lse, const float* d, void* dk,
+                            sdpa_strides_t dk_s, void* dv, sdpa_strides_t dv_s, void* dbias,
+                            sdpa_strides_t dbias_s, void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, lse, d)) != SDPA_OK)
+    return st;
+  const bool vec = p->dtype != SDPA_F32;
+  if ((st = check_tensor(p, dk, dk_s, "dk", vec)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, dv, dv_s, "dv", vec)) != SDPA_OK) return st;
+  if (dbias) {
+    if (!attn_bias) return fail(SDPA_ERR_INVALID_ARG, "dbias requires attn_bias");
+    if ((st = check_tensor(p, dbias, dbias_s, "dbias", false)) != SDPA_OK) return st;
+  }
+  sdpa::BwdArgs a{};
+  fill_bwd_args(p, a);
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o; a.lse = lse; a.dvec = (float*)d;
+  a.dk = dk; a.dv = dv; a.dbias = dbias;
+  a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
+  a.sdo_ = to_str(do_s); a.sdk_ = to_str(dk_s); a.sdv_ = to_str(dv_s); a.sdb_ = to_str(dbias_s);
+  a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
+  hipError_t e = sdpa::launch_bwd_dkdv(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0,
+                                       a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
+                          const void* k, sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
+                          const void* attn_bias, sdpa_strides_t bias_s, const void* d_o,
+                          sdpa_strides_t do_s, const float* lse, const float* d, void* dq,
+                          sdpa_strides_t dq_s, void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, lse, d)) != SDPA_OK)
+    return st;
+  if ((st = check_tensor(p, dq, dq_s, "dq", p->dtype != SDPA_F32)) != SDPA_OK) return st;
+  sdpa::BwdArgs a{};
+  fill_bwd_args(p, a);
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o; a.lse = lse; a.dvec = (float*)d;
+  a.dq = dq;
+  a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
+  a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s);
+  a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
+  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
 }  // extern "C"

@@ -63,6 +63,13 @@ _lib.sdpa_bwd.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Str
 _lib.sdpa_bwd.restype = ctypes.c_int
 _lib.sdpa_bwd_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, _vp]
 _lib.sdpa_bwd_preprocess.restype = ctypes.c_int
+_lib.sdpa_bwd_dkdv.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                               _vp, Strides, _vp, _vp, _vp, Strides, _vp, Strides, _vp, Strides,
+                               _vp]
+_lib.sdpa_bwd_dkdv.restype = ctypes.c_int
+_lib.sdpa_bwd_dq.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                             _vp, Strides, _vp, _vp, _vp, Strides, _vp]
+_lib.sdpa_bwd_dq.restype = ctypes.c_int
 _lib.sdpa_status_string.argtypes = [ctypes.c_int]
 _lib.sdpa_status_string.restype = ctypes.c_char_p
 _lib.sdpa_last_error_message.restype = ctypes.c_char_p
@@ -199,7 +206,7 @@ def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, drop
     return dq, dk, dv, dbias
 
 
-def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, b=None):
+def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, out=None):
     """D = rowsum(dO o O) in fp32: [B,H,S_q] (group mode [H, B*max_seqlen_q])."""
     group = cu_seqlens_q is not None
     p = Problem()
@@ -210,13 +217,44 @@ def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, b=None
         p.h, p.d_v = o.shape[1], o.shape[2]
         p.s_q = p.s_kv = int(max_seqlen_q)
         p.cu_seqlens_q = p.cu_seqlens_kv = cu_seqlens_q.data_ptr()
-        d = torch.empty((p.h, p.b * p.s_q), dtype=torch.float32, device=o.device)
+        shape = (p.h, p.b * p.s_q)
     else:
         p.b, p.h, p.s_q, p.d_v = o.shape
         p.s_kv = 1
-        d = torch.empty((p.b, p.h, p.s_q), dtype=torch.float32, device=o.device)
+        shape = (p.b, p.h, p.s_q)
+    d = out if out is not None else torch.empty(shape, dtype=torch.float32, device=o.device)
+    assert tuple(d.shape) == shape and d.dtype == torch.float32 and d.is_contiguous()
     p.d_qk = p.d_v
     p.scaling_factor = 1.0
     _check(_lib.sdpa_bwd_preprocess(ctypes.byref(p), _ptr(o), _strides(o, group), _ptr(dout),
                                     _strides(dout, group), _ptr(d), _stream()))
     return d
+
+
+def sdpa_bwd_dkdv(q, k, v, dout, lse, d, *, bias=None, dk=None, dv=None, dbias=None,
+                  want_dbias=False, **kw):
+    """dK, dV (and dBias) from the forward's stats and D.  Returns (dk, dv, dbias)."""
+    group = kw.get("cu_seqlens_q") is not None
+    p = make_problem(q, k, v, **kw)
+    dk = _alloc_like(k, k.shape) if dk is None else dk
+    dv = _alloc_like(v, v.shape) if dv is None else dv
+    if want_dbias and bias is not None and dbias is None:
+        dbias = _alloc_like(bias, bias.shape)
+    _check(_lib.sdpa_bwd_dkdv(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
+                              _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
+                              _ptr(dout), _strides(dout, group), _ptr(lse), _ptr(d),
+                              _ptr(dk), _strides(dk, group), _ptr(dv), _strides(dv, group),
+                              _ptr(dbias), _strides(dbias, False), _stream()))
+    return dk, dv, dbias
+
+
+def sdpa_bwd_dq(q, k, v, dout, lse, d, *, bias=None, dq=None, **kw):
+    """dQ from the forward's stats and D.  Returns dq."""
+    group = kw.get("cu_seqlens_q") is not None
+    p = make_problem(q, k, v, **kw)
+    dq = _alloc_like(q, q.shape) if dq is None else dq
+    _check(_lib.sdpa_bwd_dq(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
+                            _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
+                            _ptr(dout), _strides(dout, group), _ptr(lse), _ptr(d),
+                            _ptr(dq), _strides(dq, group), _stream()))
+    return dq

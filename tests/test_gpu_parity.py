@@ -3,7 +3,12 @@ the same seeded inputs.
 
 Tolerances (written here, used everywhere below):
   fp32 io        : max|gpu - ref| / max|ref| <= 1e-4 for every output tensor
-  bf16/fp16 io   : max|gpu - ref| <= 2e-2 on O, dQ, dK, dV
+  bf16/fp16 io   : |gpu - ref| <= 2e-2 + u |ref| elementwise on O, dQ, dK, dV,
+                   u the io unit roundoff (2^-8 bf16, 2^-11 fp16).  The u|ref|
+                   term is the rounding of the stored output itself: a bf16
+                   value in [4, 8) sits up to 0.0156 from the exact one, and
+                   dV reaches ~5 under a causal mask, so no bf16 kernel meets
+                   a flat 2e-2 there.  The strict max|gpu - ref| is printed.
   dBias (16-bit) : |gpu - ref|_ij <= 2e-2 + |dD_i| + u |ref_ij|, with u the io
                    unit roundoff (2^-8 bf16, 2^-11 fp16) and
                    dD_i = sum_e dO_ie (O_gpu - O_ref)_ie.  dBias = dS is not
@@ -64,7 +69,8 @@ def _cmp(name, got, ref, dtype, dD=None):
         scale = float(np.max(np.abs(ref))) if ref.size else 1.0
         assert err <= TOL_REL_F32 * max(scale, 1e-30), (name, err, scale)
     else:
-        assert err <= TOL_ABS_16, (name, err)
+        excess = np.abs(got - ref) - (TOL_ABS_16 + UNIT_ROUNDOFF[dtype] * np.abs(ref))
+        assert float(np.max(excess)) <= 0, (name, err, float(np.max(excess)))
     return err
 
 
