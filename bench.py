@@ -87,7 +87,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload index (2 = headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -110,7 +113,8 @@ def main():
     o = torch.empty((wl.b, wl.h, wl.s_q, wl.d_v), dtype=q.dtype, device=dev)
     lse = torch.empty((wl.b, wl.h, wl.s_q), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dvec = torch.empty((wl.b, wl.h, wl.s_q), dtype=torch.float32, device=dev)
+    n, off = S.stats_layout(wl.b, wl.h, wl.s_q)
+    stats = torch.empty(off + n, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
@@ -121,9 +125,9 @@ def main():
         launch stream bracket every kernel."""
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         calls = (lambda: S.sdpa_fwd(q, k, v, out=o, lse=lse, **kw),
-                 lambda: S.sdpa_bwd_preprocess(o, do, out=dvec),
-                 lambda: S.sdpa_bwd_dkdv(q, k, v, do, lse, dvec, dk=dk, dv=dv, **kw),
-                 lambda: S.sdpa_bwd_dq(q, k, v, do, lse, dvec, dq=dq, **kw))
+                 lambda: S.sdpa_bwd_preprocess(o, do, lse, out=stats),
+                 lambda: S.sdpa_bwd_dkdv(q, k, v, do, stats, dk=dk, dv=dv, **kw),
+                 lambda: S.sdpa_bwd_dq(q, k, v, do, stats, dq=dq, **kw))
         for i, c in enumerate(calls):
             if record:
                 e[i].record(stream)
@@ -133,6 +137,14 @@ def main():
             for i, n in enumerate(names):
                 ev[n].append((e[i], e[i + 1]))
 
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -160,7 +172,8 @@ def main():
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg[n])
     ach = per_kernel_flops[dom] / (avg[dom] * 1e-3) / 1e12
     es = 2  # bytes per io element
-    pre_bytes = 2 * wl.b * wl.h * wl.s_q * wl.d_v * es + 4 * wl.b * wl.h * wl.s_q
+    # preprocess: reads O, dO (io) and LSE, writes D and LSE*log2e (fp32)
+    pre_bytes = 2 * wl.b * wl.h * wl.s_q * wl.d_v * es + 3 * 4 * wl.b * wl.h * wl.s_q
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_traffic(dom), "avg_launch_ms": round(avg[dom], 5)}

@@ -104,7 +104,8 @@ typedef struct {
 /* Workspace.  Bytes of device scratch the caller must pass to sdpa_fwd /    */
 /* sdpa_bwd (the cuDNN glue allocates a workspace per call; the oneDNN       */
 /* backward sizes its scratchpad for D).  Returns 0 when none is needed and  */
-/* also 0 for a problem that fails validation.  Alignment: 256 bytes.        */
+/* also 0 for a problem that fails validation.  Alignment: 256 bytes.  The   */
+/* backward's workspace holds the stats described at sdpa_bwd_preprocess.    */
 /* ------------------------------------------------------------------------ */
 size_t sdpa_fwd_workspace_size(const sdpa_problem_t *problem);
 size_t sdpa_bwd_workspace_size(const sdpa_problem_t *problem);
@@ -122,8 +123,10 @@ size_t sdpa_bwd_workspace_size(const sdpa_problem_t *problem);
  *     mask hides are left unwritten.
  * Errors: SDPA_ERR_INVALID_ARG for null tensors, bad strides, p outside
  * [0,1) or half the varlen pair; SDPA_ERR_UNSUPPORTED for head dims outside
- * the compiled set (16-bit io: d_qk in {64,128,192}, d_v in {64,128};
- * fp32: d_qk, d_v <= 256), bias in group mode, keep output in group mode. */
+ * the compiled set (16-bit io: (d_qk, d_v) in {(64,64), (128,128),
+ * (192,128)}; fp32: d_qk, d_v <= 256, d_v % 4 == 0), for 16-bit tensors
+ * whose base or batch/head/seq strides are not multiples of 16 bytes or
+ * whose seq stride exceeds 16 MiB, for bias or keep output in group mode. */
 sdpa_status_t sdpa_fwd(const sdpa_problem_t *problem,
                        const void *q, sdpa_strides_t q_strides,
                        const void *k, sdpa_strides_t k_strides,
@@ -157,30 +160,32 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t *problem,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
 
-/* Backward preprocess alone: D = rowsum(dO o O) in fp32 (CK's
- * FmhaBwdOGradDotOKernel; oneDNN's backward "preprocess" kernel), written
- * densely as [b,h,s_q] (group mode [h,T_q]).  sdpa_bwd runs it itself; it is
- * exported for testing and measurement. */
+/* Backward preprocess alone (CK's FmhaBwdOGradDotOKernel; oneDNN's backward
+ * "preprocess" kernel): writes the backward stats, n = b*h*s_q floats each,
+ *   stats[0 .. n)        D = rowsum(dO o O), fp32 accumulation
+ *   stats[m .. m + n)    softmax_lse * log2(e)   (m = n rounded up to 64)
+ * in the layout of softmax_lse but with group mode rows [h, b*s_q] for both.
+ * `stats` needs sdpa_bwd_workspace_size(problem) bytes; sdpa_bwd runs this
+ * step itself into its workspace.  Errors as for sdpa_bwd. */
 sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t *problem,
                                   const void *o, sdpa_strides_t o_strides,
                                   const void *d_o, sdpa_strides_t do_strides,
-                                  float *d_out, void *stream);
+                                  const float *softmax_lse, float *stats, void *stream);
 
 /* The backward's two main kernels, one call each.  sdpa_bwd runs
  * preprocess -> dK/dV -> dQ on one stream; the dK/dV and dQ kernels read only
- * the forward's inputs and outputs and D, never each other's results, so a
- * caller may instead run sdpa_bwd_preprocess and then these two on two
- * streams, or time them one by one.  `d` is D as written by
- * sdpa_bwd_preprocess (dense fp32 [b,h,s_q], group mode [h, b*s_q]).
+ * the inputs and the stats, never each other's results, so a caller may
+ * instead run sdpa_bwd_preprocess and then these two on two streams, or time
+ * them one by one.  `stats` is the preprocess output above.
  * sdpa_bwd_dkdv writes dk, dv and (nullable) dbias; sdpa_bwd_dq writes dq.
- * Errors as for sdpa_bwd (no workspace involved). */
+ * Errors as for sdpa_bwd (no workspace argument). */
 sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t *problem,
                             const void *q, sdpa_strides_t q_strides,
                             const void *k, sdpa_strides_t k_strides,
                             const void *v, sdpa_strides_t v_strides,
                             const void *attn_bias, sdpa_strides_t bias_strides,
                             const void *d_o, sdpa_strides_t do_strides,
-                            const float *softmax_lse, const float *d,
+                            const float *stats,
                             void *dk, sdpa_strides_t dk_strides,
                             void *dv, sdpa_strides_t dv_strides,
                             void *dbias, sdpa_strides_t dbias_strides,
@@ -191,7 +196,7 @@ sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t *problem,
                           const void *v, sdpa_strides_t v_strides,
                           const void *attn_bias, sdpa_strides_t bias_strides,
                           const void *d_o, sdpa_strides_t do_strides,
-                          const float *softmax_lse, const float *d,
+                          const float *stats,
                           void *dq, sdpa_strides_t dq_strides,
                           void *stream);
 

@@ -97,6 +97,9 @@ sdpa_status_t check_tensor(const sdpa_problem_t* p, const void* ptr, sdpa_stride
     if (!ok)
       return fail(SDPA_ERR_UNSUPPORTED,
                   "%s: base pointer and batch/head/seq strides must be multiples of 16 bytes", name);
+    // tile loaders keep 32-bit byte offsets within a 128-row tile
+    if (s.seq * (int64_t)es > (int64_t)1 << 24)
+      return fail(SDPA_ERR_UNSUPPORTED, "%s: row (seq) stride above 16 MiB", name);
   }
   return SDPA_OK;
 }
@@ -131,11 +134,17 @@ sdpa::IoType io(sdpa_dtype_t t) {
 bool bias_vec_ok(const sdpa_problem_t* p, const void* bias, sdpa_strides_t s) {
   size_t es = elem_size(p->dtype);
   return bias && (uintptr_t)bias % 16 == 0 && (s.batch * es) % 16 == 0 &&
-         (s.head * es) % 16 == 0 && (s.seq * es) % 16 == 0;
+         (s.head * es) % 16 == 0 && (s.seq * es) % 16 == 0 && s.seq * (int64_t)es <= (int64_t)1 << 24;
 }
 
-size_t d_workspace_bytes(const sdpa_problem_t* p) {
+// Backward stats: D = rowsum(dO o O), then LSE * log2(e), each n floats
+// (n = b*h*s_q), the second array starting at the next 256-byte boundary.
+size_t stats_half_bytes(const sdpa_problem_t* p) {
   return align_up(sizeof(float) * (size_t)p->b * (size_t)p->h * (size_t)p->s_q);
+}
+size_t d_workspace_bytes(const sdpa_problem_t* p) { return 2 * stats_half_bytes(p); }
+float* stats_lse2(const sdpa_problem_t* p, const float* stats) {
+  return (float*)((const char*)stats + stats_half_bytes(p));
 }
 
 }  // namespace
@@ -224,21 +233,24 @@ static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
 }
 
 sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t* p, const void* o, sdpa_strides_t o_s,
-                                  const void* d_o, sdpa_strides_t do_s, float* d_out,
-                                  void* stream) {
+                                  const void* d_o, sdpa_strides_t do_s, const float* softmax_lse,
+                                  float* stats, void* stream) {
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
   if (empty_problem(p)) return SDPA_OK;
   if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
   if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
-  if (!d_out) return fail(SDPA_ERR_INVALID_ARG, "d_out is null");
+  if (!stats) return fail(SDPA_ERR_INVALID_ARG, "stats is null");
+  if (!softmax_lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null");
   if (p->d_v % (16 / (int)elem_size(p->dtype)) != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "d_v must fill whole 16-byte chunks");
   sdpa::BwdArgs a{};
   fill_bwd_args(p, a);
   a.o = o; a.dout = d_o; a.so_ = to_str(o_s); a.sdo_ = to_str(do_s);
-  a.dvec = d_out;
+  a.lse = softmax_lse;
+  a.dvec = stats;
+  a.lse2 = stats_lse2(p, stats);
   hipError_t e = sdpa::launch_bwd_pre(io(p->dtype), (int)p->d_v, a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "preprocess launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -288,6 +300,7 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o; a.dout = d_o;
   a.lse = softmax_lse;
   a.dvec = (float*)workspace;
+  a.lse2 = stats_lse2(p, (const float*)workspace);
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbias = dbias;
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.so_ = to_str(o_s); a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s); a.sdk_ = to_str(dk_s);
@@ -314,15 +327,14 @@ static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sd
                                       const void* k, sdpa_strides_t k_s, const void* v,
                                       sdpa_strides_t v_s, const void* attn_bias,
                                       sdpa_strides_t bias_s, const void* d_o, sdpa_strides_t do_s,
-                                      const float* lse, const float* d) {
+                                      const float* stats) {
   sdpa_status_t st;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
   if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;
   if ((st = check_tensor(p, v, v_s, "v", vec)) != SDPA_OK) return st;
   if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
-  if (!lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null (the backward needs the stats)");
-  if (!d) return fail(SDPA_ERR_INVALID_ARG, "d is null");
+  if (!stats) return fail(SDPA_ERR_INVALID_ARG, "stats is null (run sdpa_bwd_preprocess first)");
   if (attn_bias) {
     if (p->cu_seqlens_q) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
     if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
@@ -335,14 +347,14 @@ static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sd
 sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
                             const void* k, sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
                             const void* attn_bias, sdpa_strides_t bias_s, const void* d_o,
-                            sdpa_strides_t do_s, const float* lse, const float* d, void* dk,
+                            sdpa_strides_t do_s, const float* stats, void* dk,
                             sdpa_strides_t dk_s, void* dv, sdpa_strides_t dv_s, void* dbias,
                             sdpa_strides_t dbias_s, void* stream) {
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
   if (empty_problem(p)) return SDPA_OK;
-  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, lse, d)) != SDPA_OK)
+  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, stats)) != SDPA_OK)
     return st;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, dk, dk_s, "dk", vec)) != SDPA_OK) return st;
@@ -353,7 +365,8 @@ sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides
   }
   sdpa::BwdArgs a{};
   fill_bwd_args(p, a);
-  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o; a.lse = lse; a.dvec = (float*)d;
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o;
+  a.dvec = (float*)stats; a.lse2 = stats_lse2(p, stats);
   a.dk = dk; a.dv = dv; a.dbias = dbias;
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.sdo_ = to_str(do_s); a.sdk_ = to_str(dk_s); a.sdv_ = to_str(dv_s); a.sdb_ = to_str(dbias_s);
@@ -367,18 +380,19 @@ sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides
 sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
                           const void* k, sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s,
                           const void* attn_bias, sdpa_strides_t bias_s, const void* d_o,
-                          sdpa_strides_t do_s, const float* lse, const float* d, void* dq,
+                          sdpa_strides_t do_s, const float* stats, void* dq,
                           sdpa_strides_t dq_s, void* stream) {
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
   if (empty_problem(p)) return SDPA_OK;
-  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, lse, d)) != SDPA_OK)
+  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, stats)) != SDPA_OK)
     return st;
   if ((st = check_tensor(p, dq, dq_s, "dq", p->dtype != SDPA_F32)) != SDPA_OK) return st;
   sdpa::BwdArgs a{};
   fill_bwd_args(p, a);
-  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o; a.lse = lse; a.dvec = (float*)d;
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o;
+  a.dvec = (float*)stats; a.lse2 = stats_lse2(p, stats);
   a.dq = dq;
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s);

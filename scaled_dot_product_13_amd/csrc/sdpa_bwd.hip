@@ -27,6 +27,8 @@ namespace sdpa {
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO o O): 16 lanes per row, 16-byte loads, fp32 accumulation.
+// The same pass also stores LSE * log2(e) beside D, so that the main kernels
+// form P = exp2(scale*log2e * S - LSE*log2e) with one FMA per element.
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
@@ -59,8 +61,12 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
   if (ok && sub == 0) {
-    int64_t base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+    const int64_t base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
     a.dvec[base + row] = acc;
+    if (a.lse2) {
+      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      a.lse2[base + row] = a.lse[lb + row] * kLog2e;
+    }
   }
 }
 
@@ -73,33 +79,36 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
 //   dV^T += dO^T (P o Z)   and   dK^T += Q^T dS
 // directly as B operands; the A operands dO^T and Q^T come from the same LDS
 // tiles through the transposing LDS read.
-template <int DQK, int DV, bool DROP> struct DkdvOcc {
-  static constexpr int value = 1;
-};
-
 template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
-  constexpr int BC = 128, BQ = 64;
+  constexpr int BC = 128, BQ = 32, QBLK = BQ / 32;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
-  // double-buffered Q, dO, LSE and D tiles, plus (aligned bias) the bias tile
-  __shared__ __attribute__((aligned(1024))) T sQ[2][BQ * DQK];
-  __shared__ __attribute__((aligned(1024))) T sO[2][BQ * DV];
-  __shared__ __attribute__((aligned(1024))) T sB[BIAS ? 2 : 1][BIAS ? BQ * BC : 64];
-  __shared__ __attribute__((aligned(256))) float sL[2][BQ], sD[2][BQ];
+  // Query tiles are triple-buffered: while tile i is consumed (elementwise
+  // step, dV and dK products) the S and dP products of tile i+1 are issued
+  // and tile i+2 is loading.  The bias tile joins them through LDS when it
+  // fits (d_qk <= 128).
+  constexpr int NB = 3;
+  constexpr bool BIAS_LDS = BIAS && DQK <= 128;
+  __shared__ __attribute__((aligned(1024))) T sQ[NB][BQ * DQK];
+  __shared__ __attribute__((aligned(1024))) T sO[NB][BQ * DV];
+  __shared__ __attribute__((aligned(1024))) T sB[BIAS_LDS ? NB : 1][BIAS_LDS ? BQ * BC : 64];
+  __shared__ __attribute__((aligned(256))) float sL[NB][BQ], sD[NB][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = wave_id();
+  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H, a.B);
+  if (!wi.valid) return;
+  const int b = wi.b, h = wi.h;
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
-  const int kv0 = blockIdx.x * BC;
+  const int kv0 = wi.tile * BC;  // causal: key tile 0 has the most query tiles
   if (kv0 >= skv) return;
 
   const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
   const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
   const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
   const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
-  const int64_t lse_base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
-  const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+  const int64_t st_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
   const uint16_t* bg = nullptr;
   uint16_t* dbg = nullptr;
   if (BIAS) {
@@ -107,7 +116,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
     if (a.dbias) dbg = (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
   }
 
-  const int kvr = kv0 + 32 * w + l32;  // this lane's key
+  const int wk0 = kv0 + 32 * w;        // this wave's first key
+  const int kvr = wk0 + l32;           // this lane's key
   const bool kv_ok = kvr < skv;
   u32x4 kreg[KT], vreg[VT];
 #pragma unroll
@@ -121,6 +131,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
   const uint32_t bh = (uint32_t)(b * a.H + h);
   if (DROP) dk = drop_key(a.drop);
   const float rescale = DROP ? a.drop.rescale : 1.f;
+  const float c = a.scale_log2;
 
   f32x16 dkacc[QB], dvacc[VB];
 #pragma unroll
@@ -130,6 +141,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
 
   // causal: query rows below kv0 see none of these keys
   const int q_begin = CAUSAL ? (kv0 / BQ) * BQ : 0;
+  const int nq = sq > q_begin ? (sq - q_begin + BQ - 1) / BQ : 0;
   if (CAUSAL && dbg && kv_ok) {
     // dBias is zero wherever the mask hides the key: rows [0, q_begin)
     for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
@@ -137,128 +149,173 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
 
   // bias tiles come through LDS when the whole 64 x 128 tile is in range and
   // its rows are 16-byte aligned; otherwise each lane reads its elements.
-  const bool bias_lds = BIAS && a.bias_vec && kv0 + BC <= skv;
-  const T* dog_ = dog;
-  const float* lseg = a.lse + lse_base;
-  const float* dvg = a.dvec + d_base;
-  auto issue = [&](int q0, int buf) {
-    tile_load_direct<DQK, BQ>(sQ[buf], qg, a.sq_.s, q0, sq, w, lane);
-    tile_load_direct<DV, BQ>(sO[buf], dog_, a.sdo_.s, q0, sq, w, lane);
-    if (BIAS && bias_lds)
-      tile_load_direct<BC, BQ>(sB[buf], (const T*)(bg + kv0), a.sb_.s, q0, sq, w, lane);
-    // the 64 fp32 LSE (wave 0) and D (wave 1) values, one row per lane,
+  const bool bias_lds = BIAS_LDS && a.bias_vec && kv0 + BC <= skv;
+  TileLoader<DQK, BQ, T> ldQ;
+  TileLoader<DV, BQ, T> ldO;
+  TileLoader<BC, BQ, T> ldB;
+  ldQ.init(qg, a.sq_.s, w, lane);
+  ldO.init(dog, a.sdo_.s, w, lane);
+  if (BIAS_LDS && bias_lds) ldB.init((const T*)(bg + kv0), a.sb_.s, w, lane);
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ, buf = i % NB;
+    ldQ.load(sQ[buf], q0, sq, w, lane);
+    ldO.load(sO[buf], q0, sq, w, lane);
+    if (BIAS_LDS && bias_lds) ldB.load(sB[buf], q0, sq, w, lane);
+    // the 64 LSE*log2(e) (wave 0) and D (wave 1) values, one row per lane,
     // rows clamped to the sequence
-    if (w < 2) {
+    if (w < 2 && lane < BQ) {
       int r = q0 + lane;
       r = r < sq ? r : sq - 1;
-      const float* src = (w == 0 ? lseg : dvg) + r;
+      const float* src = (w == 0 ? a.lse2 : a.dvec) + st_base + r;
       float* dst = w == 0 ? sL[buf] : sD[buf];
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
+  auto tile_active = [&](int i) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ;
+    return wk0 < skv && (!CAUSAL || q0 + BQ - 1 >= wk0);
+  };
+  auto tile_needs_mask = [&](int i) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ;
+    return (q0 + BQ > sq) || (wk0 + 31 >= skv) || (CAUSAL && q0 < wk0 + 31);
+  };
 
-  if (q_begin < sq) issue(q_begin, 0);
-  int it = 0;
-  for (int q0 = q_begin; q0 < sq; q0 += BQ, ++it) {
-    const int buf = it & 1;
-    wait_all();
-    __syncthreads();
-    const T* cQ = sQ[buf];
-    const T* cO = sO[buf];
+  // S = Q K^T and dP = dO V^T of tile i (queries in sig order)
+  auto products = [&](int i, f32x16* s, f32x16* dp) __attribute__((always_inline)) {
+    const T* cQ = sQ[i % NB];
+    const T* cO = sO[i % NB];
+#pragma unroll
+    for (int qb = 0; qb < QBLK; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int qb = 0; qb < QBLK; ++qb)
+        s[qb] = mfma32<T>(lds_rowA<DQK>(cQ, 32 * qb, 16 * t, lane), kreg[t], s[qb]);
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int qb = 0; qb < QBLK; ++qb)
+        dp[qb] = mfma32<T>(lds_rowA<DV>(cO, 32 * qb, 16 * t, lane), vreg[t], dp[qb]);
+  };
+
+  // elementwise step of tile i: P (dropped out) and dS into B-operand form
+  auto elementwise = [&](bool need_mask, int i, const f32x16* s, const f32x16* dp, u32x4* pb,
+                         u32x4* dsb) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ, buf = i % NB;
     const float* cL = sL[buf];
     const float* cD = sD[buf];
-    const T* cB = sB[BIAS ? buf : 0];
-    if (q0 + BQ < sq) issue(q0 + BQ, buf ^ 1);
-
-    // causal: this wave's keys are all above the last row of the tile
-    const bool active = kv0 + 32 * w < skv && (!CAUSAL || q0 + BQ - 1 >= kv0 + 32 * w);
-    if (!active) {
-      if (CAUSAL && dbg && kv_ok)  // the whole tile is hidden from my key
-        for (int i = q0 + g; i < min(q0 + BQ, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
-      continue;
-    }
-
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      u32x4 a0 = lds_rowA<DQK>(cQ, 0, 16 * t, lane);
-      u32x4 a1 = lds_rowA<DQK>(cQ, 32, 16 * t, lane);
-      s[0] = mfma32<T>(a0, kreg[t], s[0]);
-      s[1] = mfma32<T>(a1, kreg[t], s[1]);
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      u32x4 a0 = lds_rowA<DV>(cO, 0, 16 * t, lane);
-      u32x4 a1 = lds_rowA<DV>(cO, 32, 16 * t, lane);
-      dp[0] = mfma32<T>(a0, vreg[t], dp[0]);
-      dp[1] = mfma32<T>(a1, vreg[t], dp[1]);
-    }
-
+    const T* cB = sB[BIAS_LDS ? buf : 0];
     uint32_t kw[8];
     if (DROP) {
+      // 4x4 patches along this lane's queries: 8 per 64 rows (the second
+      // half unused when the tile has 32 rows)
       uint32_t var4[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
       quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
     }
+#pragma unroll
+    for (int qb = 0; qb < QBLK; ++qb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int lb = 32 * qb + 16 * hh + 8 * g;  // first of my 8 consecutive rows
+        const f32x4 L0 = *(const f32x4*)(cL + lb), L1 = *(const f32x4*)(cL + lb + 4);
+        const f32x4 D0 = *(const f32x4*)(cD + lb), D1 = *(const f32x4*)(cD + lb + 4);
+        float pv[8], dv_[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hh + e;
+          const int ql = lb + e, qr = q0 + ql;
+          const float L = e < 4 ? L0[e] : L1[e - 4];
+          const float Dq = e < 4 ? D0[e] : D1[e - 4];
+          float off = -L;  // exponent = scale*log2e*s + log2e*bias - LSE*log2e
+          if (BIAS) {
+            float bval = 0.f;
+            if (bias_lds)
+              bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * w + l32)));
+            else if (kv_ok && qr < sq)
+              bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
+            off = __builtin_fmaf(bval, kLog2e, off);
+          }
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, off));
+          if (need_mask) {
+            const bool vis = qr < sq && kv_ok && (!CAUSAL || kvr <= qr);
+            p = vis ? p : 0.f;
+          }
+          float z = 1.f, pz = p;
+          if (DROP) {
+            const int k = 4 * qb + 2 * hh + (e >> 2);
+            const bool keep = ((kw[k] >> (8 * (e & 3))) & 0xffu) >= dk.thr;
+            z = keep ? rescale : 0.f;
+            pz = keep ? p : 0.f;
+          }
+          const float ds = p * (dp[qb][r] * z - Dq);
+          if (BIAS && dbg && kv_ok && qr < sq)
+            dbg[(int64_t)qr * a.sdb_.s + kvr] = (uint16_t)(pack2<T>(ds, 0.f) & 0xffffu);
+          pv[e] = pz;
+          dv_[e] = ds;
+        }
+        const int tt = 2 * qb + hh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[tt][e] = pack2<T>(pv[2 * e], pv[2 * e + 1]);
+          dsb[tt][e] = pack2<T>(dv_[2 * e], dv_[2 * e + 1]);
+        }
+      }
+    }
+  };
+  // dV^T += dO^T (P o Z) and dK^T += Q^T dS for tile i
+  auto dvdk = [&](int i, const u32x4* pb, const u32x4* dsb) __attribute__((always_inline)) {
+    const T* cQ = sQ[i % NB];
+    const T* cO = sO[i % NB];
+#pragma unroll
+    for (int tt = 0; tt < 2 * QBLK; ++tt) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+        dvacc[vb] = mfma32<T>(lds_trA<DV>(cO, 16 * tt, 32 * vb, lane), pb[tt], dvacc[vb]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        dkacc[qb] = mfma32<T>(lds_trA<DQK>(cQ, 16 * tt, 32 * qb, lane), dsb[tt], dkacc[qb]);
+    }
+  };
+  // One pipelined step: the products of tile i+1 are issued before the
+  // elementwise work and the dV / dK products of tile i, so the matrix cores
+  // have independent work while the vector unit runs.
+  auto run = [&](int i, const f32x16* cs, const f32x16* cdp, f32x16* ns, f32x16* ndp)
+      __attribute__((always_inline)) {
+    if (i + 1 < nq && tile_active(i + 1)) products(i + 1, ns, ndp);
+    if (tile_active(i)) {
+      u32x4 pb[2 * QBLK], dsb[2 * QBLK];
+      elementwise(tile_needs_mask(i), i, cs, cdp, pb, dsb);
+      dvdk(i, pb, dsb);
+    } else {
+      const int q0 = q_begin + i * BQ;  // the whole tile is hidden from my key
+      if (CAUSAL && dbg && kv_ok)
+        for (int r = q0 + g; r < min(q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+    }
+  };
 
-    const bool need_mask = (q0 + BQ > sq) || !kv_ok || (kv0 + 32 * w + 31 >= skv) ||
-                           (CAUSAL && q0 < kv0 + 32 * w + 31);
-    u32x4 pb[4], dsb[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qb + 16 * (r >> 3) + 8 * g + (r & 7);  // local query row
-        const int qr = q0 + ql;
-        float x = s[qb][r] * a.scale_log2 - cL[ql] * kLog2e;
-        if (BIAS) {
-          float bval = 0.f;
-          if (bias_lds)
-            bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * w + l32)));
-          else if (kv_ok && qr < sq)
-            bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
-          x += bval * kLog2e;
-        }
-        const bool vis = !need_mask || (qr < sq && kv_ok && (!CAUSAL || kvr <= qr));
-        float p = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
-        float z = 1.f, pz = p;
-        if (DROP) {
-          int k = 4 * qb + 2 * (r >> 3) + ((r & 7) >> 2);
-          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
-          z = keep ? rescale : 0.f;
-          pz = keep ? p : 0.f;
-        }
-        const float ds = vis ? p * (dp[qb][r] * z - cD[ql]) : 0.f;  // hidden: exactly 0
-        s[qb][r] = pz;
-        dp[qb][r] = ds;
-        if (BIAS && dbg && kv_ok && qr < sq) {
-          uint16_t bits = (uint16_t)(pack2<T>(ds, 0.f) & 0xffffu);
-          dbg[(int64_t)qr * a.sdb_.s + kvr] = bits;
-        }
+  if (nq > 0) {
+    issue(0);
+    if (nq > 1) issue(1);
+    wait_all();
+    __syncthreads();
+    f32x16 sA[QBLK], dA[QBLK], sB_[QBLK], dB_[QBLK];
+    if (tile_active(0)) products(0, sA, dA);
+    // two iterations per trip so that the current / next accumulators swap
+    // roles without register copies
+    for (int i = 0; i < nq; i += 2) {
+      if (i > 0) {
+        wait_all();
+        __syncthreads();
       }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      int qb = tt >> 1, r0 = 8 * (tt & 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[tt][e] = pack2<T>(s[qb][r0 + 2 * e], s[qb][r0 + 2 * e + 1]);
-        dsb[tt][e] = pack2<T>(dp[qb][r0 + 2 * e], dp[qb][r0 + 2 * e + 1]);
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        u32x4 av = lds_trA<DV>(cO, 16 * tt, 32 * vb, lane);
-        dvacc[vb] = mfma32<T>(av, pb[tt], dvacc[vb]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        u32x4 aq = lds_trA<DQK>(cQ, 16 * tt, 32 * qb, lane);
-        dkacc[qb] = mfma32<T>(aq, dsb[tt], dkacc[qb]);
-      }
+      if (i + 2 < nq) issue(i + 2);
+      run(i, sA, dA, sB_, dB_);
+      if (i + 1 >= nq) break;
+      wait_all();
+      __syncthreads();
+      if (i + 3 < nq) issue(i + 3);
+      run(i + 1, sB_, dB_, sA, dA);
     }
   }
 
@@ -308,9 +365,13 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];
   __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = wave_id();
+  const int nqt = (a.seq.s_q + BR - 1) / BR;
+  const WorkItem wi = xcd_work(nqt, a.H, a.B);
+  if (!wi.valid) return;
+  const int b = wi.b, h = wi.h;
+  const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
   const int q0 = mt * BR;
@@ -337,8 +398,9 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     doreg[t] = row_ok ? *(const u32x4*)(dog + (int64_t)row * a.sdo_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
   float lse2 = 0.f, Drow = 0.f;
   if (row_ok) {
-    lse2 = a.lse[row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0) + row] * kLog2e;
-    Drow = a.dvec[row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + row];
+    const int64_t st = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + row;
+    lse2 = a.lse2[st];
+    Drow = a.dvec[st];
   }
 
   DropKey dk{};
@@ -350,9 +412,13 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
 #pragma unroll
   for (int i = 0; i < QB; ++i) dqacc[i] = f32x16{};
 
+  TileLoader<DQK, BC, T> ldK;
+  TileLoader<DV, BC, T> ldV;
+  ldK.init(kg, a.sk_.s, w, lane);
+  ldV.init(vg, a.sv_.s, w, lane);
   if (nt > 0) {
-    tile_load_direct<DQK, BC>(sK[0], kg, a.sk_.s, 0, skv, w, lane);
-    tile_load_direct<DV, BC>(sV[0], vg, a.sv_.s, 0, skv, w, lane);
+    ldK.load(sK[0], 0, skv, w, lane);
+    ldV.load(sV[0], 0, skv, w, lane);
   }
   for (int it = 0; it < nt; ++it) {
     const int n0 = it * BC;
@@ -383,8 +449,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     }
 
     if (it + 1 < nt) {
-      tile_load_direct<DQK, BC>(sK[(it + 1) & 1], kg, a.sk_.s, n0 + BC, skv, w, lane);
-      tile_load_direct<DV, BC>(sV[(it + 1) & 1], vg, a.sv_.s, n0 + BC, skv, w, lane);
+      ldK.load(sK[(it + 1) & 1], n0 + BC, skv, w, lane);
+      ldV.load(sV[(it + 1) & 1], n0 + BC, skv, w, lane);
     }
     if (!active) continue;
 
@@ -490,8 +556,9 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
   const uint32_t bh = (uint32_t)(b * a.H + h);
-  const float lse = a.lse[row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0) + i];
-  const float Di = a.dvec[row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + i];
+  const int64_t st = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + i;
+  const float lse2 = a.lse2[st];
+  const float Di = a.dvec[st];
   float q[4], dO[4], acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -514,7 +581,7 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
     }
     float s = wave_sum(ps) * a.scale + (BIAS ? brow[j] : 0.f);
     float dp = wave_sum(pd);
-    float p = expf(s - lse);
+    float p = exp2f(s * kLog2e - lse2);
     float z = 1.f;
     if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
     float ds = p * (dp * z - Di);
@@ -549,7 +616,6 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
   const uint32_t bh = (uint32_t)(b * a.H + h);
-  const int64_t lse_base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
   const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
   float k[4], v[4], gk[4], gv[4];
 #pragma unroll
@@ -575,7 +641,7 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
     }
     float s = wave_sum(ps) * a.scale + (BIAS ? bcol[(int64_t)i * a.sb_.s] : 0.f);
     float dp = wave_sum(pd);
-    float p = expf(s - a.lse[lse_base + i]);
+    float p = exp2f(s * kLog2e - a.lse2[d_base + i]);
     float z = 1.f;
     if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
     float ds = p * (dp * z - a.dvec[d_base + i]);
@@ -618,7 +684,7 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
 
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
-  dim3 grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(256);
+  dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(256);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)
 #undef L
@@ -626,7 +692,7 @@ static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a,
 }
 template <typename T, int DQK, int DV>
 static hipError_t dq_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
-  dim3 grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
+  dim3 grid = xcd_grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)
 #undef L

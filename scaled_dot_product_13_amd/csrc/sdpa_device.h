@@ -20,6 +20,7 @@ namespace sdpa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -110,27 +111,59 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at LDS base +
 // 16 l).  Each of the 4 waves issues ROWS*D/8/256 such loads; lane l of load
 // j covers physical chunk 64(4j + w) + l of the tile, and fetches the logical
-// chunk that the swizzle puts there.  Rows at or beyond `row_limit` are
-// clamped to row_limit - 1 (callers mask them), so every address is valid;
-// row_limit must be >= 1.
-template <int D, int ROWS, typename T>
-__device__ __forceinline__ void tile_load_direct(T* tile, const T* g, int64_t row_stride, int row0,
-                                                 int row_limit, int w, int lane) {
-  constexpr int CPR = Lds<D>::CPR;
-  constexpr int PER_WAVE = ROWS * CPR / 256;
+// chunk that the swizzle puts there.  The per-lane byte offsets within a
+// full tile are computed once; the tile's first row only moves a uniform
+// base.  A tile that runs past `row_limit` takes a slow path that clamps rows
+// to row_limit - 1 (callers mask those rows), so every address is valid;
+// row_limit must be >= 1.  `w` must be wave-uniform.
+template <int D, int ROWS, typename T> struct TileLoader {
+  static constexpr int CPR = Lds<D>::CPR;
+  static constexpr int PER_WAVE = ROWS * CPR / 256;
   static_assert(ROWS * CPR % 256 == 0, "tile must split into whole wave loads");
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
+  static constexpr int LOWMASK = (D % 128 == 0) ? 15 : 7;
+  const char* g;
+  int64_t stride_b;  // row stride in bytes
+  uint32_t voff[PER_WAVE];
+
+  __device__ __forceinline__ static void coords(int j, int w, int lane, int& row, int& c) {
     const int L = 64 * (4 * j + w) + lane;
-    const int row = L / CPR, phys = L % CPR;
-    const int c = (phys & ~((D % 128 == 0) ? 15 : 7)) | ((phys ^ Lds<D>::swz(row)) & ((D % 128 == 0) ? 15 : 7));
-    int gr = row0 + row;
-    gr = gr < row_limit ? gr : row_limit - 1;
-    const T* src = g + (int64_t)gr * row_stride + 8 * c;
-    T* dst = tile + 512 * (4 * j + w);  // 1 KiB per wave load
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    row = L / CPR;
+    const int phys = L % CPR;
+    c = (phys & ~LOWMASK) | ((phys ^ Lds<D>::swz(row)) & LOWMASK);
   }
-}
+  __device__ __forceinline__ void init(const T* g_, int64_t row_stride, int w, int lane) {
+    g = (const char*)g_;
+    stride_b = row_stride * (int64_t)sizeof(T);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      int row, c;
+      coords(j, w, lane, row, c);
+      voff[j] = (uint32_t)(row * stride_b + 16 * c);
+    }
+  }
+  __device__ __forceinline__ void load(T* tile, int row0, int row_limit, int w, int lane) const {
+    if (row0 + ROWS <= row_limit) {
+      const char* base = g + row0 * stride_b;
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(base + voff[j]),
+                                         (lds_void*)(tile + 512 * (4 * j + w)), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        int row, c;
+        coords(j, w, lane, row, c);
+        int gr = row0 + row;
+        gr = gr < row_limit ? gr : row_limit - 1;
+        __builtin_amdgcn_global_load_lds((const void*)(g + gr * stride_b + 16 * c),
+                                         (lds_void*)(tile + 512 * (4 * j + w)), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// wave index as a scalar (the compiler cannot prove threadIdx.x >> 6 uniform)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Wait for all of this wave's outstanding memory operations (including the
 // direct-to-LDS loads) to complete; a barrier after it publishes the tile.

@@ -31,29 +31,45 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   constexpr int BR = 128, BC = 64;
   constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
   constexpr int DB = DV / 32;   // 32-wide blocks of d_v
+  // Lazy rescaling: the running max is only raised (and O, l rescaled) when
+  // some row's max grows by more than TAU (log2 units); until then the
+  // probabilities are exp2(x - m_run) <= 2^TAU, exact in fp32 and bf16.
+  constexpr float TAU = 8.f;
   __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];  // double-buffered tiles
   __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int mt = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;  // heavy first
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = wave_id();
+  const int nqt = (a.seq.s_q + BR - 1) / BR;
+  const WorkItem wi = xcd_work(nqt, a.H, a.B);
+  if (!wi.valid) return;
+  const int b = wi.b, h = wi.h;
+  const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
   const int q0 = mt * BR;
   if (q0 >= sq) return;
 
   const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
-  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
-  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
   T* og = base_ptr_mut<T>(a.o, a.so_, sp, h, true);
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
 
   const int kv_end = CAUSAL ? min(skv, q0 + BR) : skv;
   const int nt = (kv_end + BC - 1) / BC;
-
-  const int row = q0 + 32 * w + l32;  // this lane's query row
+  const int wq0 = q0 + 32 * w;        // this wave's first query row
+  const int row = wq0 + l32;          // this lane's query row
   const bool row_ok = row < sq;
+
+  TileLoader<DQK, BC, T> ldK;
+  TileLoader<DV, BC, T> ldV;
+  ldK.init(base_ptr<T>(a.k, a.sk_, sp, h, false), a.sk_.s, w, lane);
+  ldV.init(base_ptr<T>(a.v, a.sv_, sp, h, false), a.sv_.s, w, lane);
+  if (nt > 0) {
+    ldK.load(sK[0], 0, skv, w, lane);
+    ldV.load(sV[0], 0, skv, w, lane);
+  }
+
   u32x4 qreg[KT];
 #pragma unroll
   for (int t = 0; t < KT; ++t)
@@ -61,18 +77,16 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
                      : u32x4{0, 0, 0, 0};
 
   DropKey dk{};
-  uint32_t bh = (uint32_t)(b * a.H + h);
+  const uint32_t bh = (uint32_t)(b * a.H + h);
   if (DROP) dk = drop_key(a.drop);
+  const float c = a.scale_log2;
+  const bool pos = c >= 0.f;  // uniform: which extreme of the raw scores is the max
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -1e30f, l_run = 0.f;  // m_run in scaled log2 units
 
-  if (nt > 0) {
-    tile_load_direct<DQK, BC>(sK[0], kg, a.sk_.s, 0, skv, w, lane);
-    tile_load_direct<DV, BC>(sV[0], vg, a.sv_.s, 0, skv, w, lane);
-  }
   for (int it = 0; it < nt; ++it) {
     const int n0 = it * BC;
     const T* cK = sK[it & 1];
@@ -81,7 +95,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     __syncthreads();  // ... and everyone's; tile it-1 is fully consumed
 
     // a wave whose rows see none of this tile skips it (causal)
-    const bool active = !CAUSAL || (n0 <= q0 + 32 * w + 31);
+    const bool active = !CAUSAL || n0 <= wq0 + 31;
 
     // bias for this lane's row: 4 runs of 8 consecutive keys (issued before
     // the next tile's prefetch so that waiting for them does not wait for it)
@@ -105,8 +119,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       }
     }
     if (it + 1 < nt) {
-      tile_load_direct<DQK, BC>(sK[(it + 1) & 1], kg, a.sk_.s, n0 + BC, skv, w, lane);
-      tile_load_direct<DV, BC>(sV[(it + 1) & 1], vg, a.sv_.s, n0 + BC, skv, w, lane);
+      ldK.load(sK[(it + 1) & 1], n0 + BC, skv, w, lane);
+      ldV.load(sV[(it + 1) & 1], n0 + BC, skv, w, lane);
     }
     if (!active) continue;
 
@@ -129,37 +143,76 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       quad_keep_words<true>(var4, (uint32_t)row >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
     }
 
-    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
-    float mloc = -INFINITY;
+    // Scores in scaled log2 units.  Without bias the scale is folded into
+    // the exponent's FMA and the row max is taken on the raw scores.
+    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > wq0);
+    auto visible = [&](int blk, int r) {
+      int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+      return kv < skv && (!CAUSAL || kv <= row);
+    };
+    float mrow;
+    if (BIAS) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[blk][r] * a.scale_log2;
-        if (BIAS) {
+        for (int r = 0; r < 16; ++r) {
           int u = 2 * blk + (r >> 3), e = r & 7;
           uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          x += to_f32<T>((uint16_t)bits) * kLog2e;
+          s[blk][r] = __builtin_fmaf(s[blk][r], c, to_f32<T>((uint16_t)bits) * kLog2e);
         }
-        if (need_mask) {
-          int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-          bool vis = kv < skv && (!CAUSAL || kv <= row);
-          x = vis ? x : -INFINITY;
-        }
-        s[blk][r] = x;
-        mloc = fmaxf(mloc, x);
+      if (need_mask) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+      mrow = max_pair32(mx);
+    } else {
+      const float hide = pos ? -INFINITY : INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : hide;
+      }
+      float mx = -INFINITY, mn = INFINITY;
+      if (pos) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+        mx = max_pair32(mx);
+        mrow = mx == -INFINITY ? -INFINITY : mx * c;
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mn = fminf(mn, s[blk][r]);
+        mn = -max_pair32(-mn);
+        mrow = mn == INFINITY ? -INFINITY : mn * c;
       }
     }
-    const float m_new = fmaxf(m_run, max_pair32(mloc));
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float m_new = fmaxf(m_run, mrow);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
-    u32x4 pb[4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(s[blk][r] - m_use);
+        float pv = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
+                        : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_run));
+        if (!BIAS && need_mask) pv = visible(blk, r) ? pv : 0.f;
         psum += pv;
         if (DROP) {
           int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
@@ -169,16 +222,14 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
         s[blk][r] = pv;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
+    u32x4 pb[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       int blk = tt >> 1, r0 = 8 * (tt & 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
     }
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
 
     if (DROP && a.keep && row_ok) {
       uint8_t* kp = a.keep + (((int64_t)b * a.H + h) * a.seq.s_q + row) * a.seq.s_kv;
@@ -302,7 +353,7 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
 template <typename T, int DQK, int DV>
 static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const FwdArgs& a,
                                      hipStream_t st) {
-  dim3 grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
+  dim3 grid = xcd_grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
 #define SDPA_FWD_CASE(C, BI, DR)                                                 \
   if (causal == C && bias == BI && drop == DR) {                                 \
     hipLaunchKernelGGL((fwd_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); \

@@ -48,6 +48,32 @@ __device__ __forceinline__ int64_t row_stat_base(const SeqInfo& s, const SeqPos&
   return ((int64_t)b * H + h) * s.s_q;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  The tile kernels use a 1-D grid and give XCD x a contiguous range of
+// the (batch*head, tile) work list, so all tiles of one head - which read the
+// same K/V (or Q/dO) tiles - run behind one L2.  Any bijection is correct;
+// this one only changes which L2 serves which head.
+struct WorkItem {
+  int b, h, tile;
+  bool valid;
+};
+__device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B) {
+  const int total = ntiles * H * B;
+  const int lin = blockIdx.x, per = (total + 7) / 8;
+  const int logical = (lin & 7) * per + (lin >> 3);
+  WorkItem wi;
+  wi.valid = logical < total;
+  const int hb = logical / ntiles;
+  wi.tile = logical - hb * ntiles;
+  wi.b = hb / H;
+  wi.h = hb - wi.b * H;
+  return wi;
+}
+inline dim3 xcd_grid(int ntiles, int H, int B) {
+  const long total = (long)ntiles * H * B;
+  return dim3((unsigned)((total + 7) / 8 * 8), 1, 1);
+}
+
 struct DropKey {
   uint32_t k0, k1, off, thr;
 };

@@ -47,8 +47,11 @@ struct FwdArgs {
 
 struct BwdArgs {
   const void *q, *k, *v, *bias, *o, *dout;
-  const float* lse;
-  float* dvec;      // D workspace: batch [B,H,S_q]; group [H, B*S_q]
+  const float* lse;  // forward stats (natural log), read by the preprocess only
+  // backward stats written by the preprocess: D and LSE*log2(e), each dense
+  // batch [B,H,S_q] or group [H, B*S_q]
+  float* dvec;
+  float* lse2;
   void *dq, *dk, *dv, *dbias;
   Str sq_, sk_, sv_, sb_, so_, sdo_, sdq_, sdk_, sdv_, sdb_;
   int32_t bias_vec;

@@ -61,14 +61,13 @@ _lib.sdpa_bwd.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Str
                           _vp, Strides, _vp, Strides, _vp, _vp, Strides, _vp, Strides,
                           _vp, Strides, _vp, Strides, _vp, _sz, _vp]
 _lib.sdpa_bwd.restype = ctypes.c_int
-_lib.sdpa_bwd_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, _vp]
+_lib.sdpa_bwd_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, _vp, _vp]
 _lib.sdpa_bwd_preprocess.restype = ctypes.c_int
 _lib.sdpa_bwd_dkdv.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
-                               _vp, Strides, _vp, _vp, _vp, Strides, _vp, Strides, _vp, Strides,
-                               _vp]
+                               _vp, Strides, _vp, _vp, Strides, _vp, Strides, _vp, Strides, _vp]
 _lib.sdpa_bwd_dkdv.restype = ctypes.c_int
 _lib.sdpa_bwd_dq.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
-                             _vp, Strides, _vp, _vp, _vp, Strides, _vp]
+                             _vp, Strides, _vp, _vp, Strides, _vp]
 _lib.sdpa_bwd_dq.restype = ctypes.c_int
 _lib.sdpa_status_string.argtypes = [ctypes.c_int]
 _lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -206,8 +205,17 @@ def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, drop
     return dq, dk, dv, dbias
 
 
-def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, out=None):
-    """D = rowsum(dO o O) in fp32: [B,H,S_q] (group mode [H, B*max_seqlen_q])."""
+def stats_layout(b, h, s_q):
+    """(n, offset) of the backward stats: D at [0, n), LSE*log2(e) at
+    [offset, offset + n) floats (offset = n rounded up to 64 floats)."""
+    n = b * h * s_q
+    return n, (n + 63) // 64 * 64
+
+
+def sdpa_bwd_preprocess(o, dout, lse, *, cu_seqlens_q=None, max_seqlen_q=None, out=None):
+    """Backward stats: a flat fp32 tensor holding D = rowsum(dO o O) and
+    LSE*log2(e) (see stats_layout); returns it.  D alone is
+    stats[:n] viewed as [B,H,S_q] (group mode [H, B*max_seqlen_q])."""
     group = cu_seqlens_q is not None
     p = Problem()
     p.struct_size = ctypes.sizeof(Problem)
@@ -217,23 +225,22 @@ def sdpa_bwd_preprocess(o, dout, *, cu_seqlens_q=None, max_seqlen_q=None, out=No
         p.h, p.d_v = o.shape[1], o.shape[2]
         p.s_q = p.s_kv = int(max_seqlen_q)
         p.cu_seqlens_q = p.cu_seqlens_kv = cu_seqlens_q.data_ptr()
-        shape = (p.h, p.b * p.s_q)
     else:
         p.b, p.h, p.s_q, p.d_v = o.shape
         p.s_kv = 1
-        shape = (p.b, p.h, p.s_q)
-    d = out if out is not None else torch.empty(shape, dtype=torch.float32, device=o.device)
-    assert tuple(d.shape) == shape and d.dtype == torch.float32 and d.is_contiguous()
     p.d_qk = p.d_v
     p.scaling_factor = 1.0
+    n, off = stats_layout(p.b, p.h, p.s_q)
+    d = out if out is not None else torch.empty(off + n, dtype=torch.float32, device=o.device)
+    assert d.numel() >= off + n and d.dtype == torch.float32 and d.is_contiguous()
     _check(_lib.sdpa_bwd_preprocess(ctypes.byref(p), _ptr(o), _strides(o, group), _ptr(dout),
-                                    _strides(dout, group), _ptr(d), _stream()))
+                                    _strides(dout, group), _ptr(lse), _ptr(d), _stream()))
     return d
 
 
-def sdpa_bwd_dkdv(q, k, v, dout, lse, d, *, bias=None, dk=None, dv=None, dbias=None,
+def sdpa_bwd_dkdv(q, k, v, dout, stats, *, bias=None, dk=None, dv=None, dbias=None,
                   want_dbias=False, **kw):
-    """dK, dV (and dBias) from the forward's stats and D.  Returns (dk, dv, dbias)."""
+    """dK, dV (and dBias) from the backward stats.  Returns (dk, dv, dbias)."""
     group = kw.get("cu_seqlens_q") is not None
     p = make_problem(q, k, v, **kw)
     dk = _alloc_like(k, k.shape) if dk is None else dk
@@ -242,19 +249,19 @@ def sdpa_bwd_dkdv(q, k, v, dout, lse, d, *, bias=None, dk=None, dv=None, dbias=N
         dbias = _alloc_like(bias, bias.shape)
     _check(_lib.sdpa_bwd_dkdv(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
                               _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
-                              _ptr(dout), _strides(dout, group), _ptr(lse), _ptr(d),
+                              _ptr(dout), _strides(dout, group), _ptr(stats),
                               _ptr(dk), _strides(dk, group), _ptr(dv), _strides(dv, group),
                               _ptr(dbias), _strides(dbias, False), _stream()))
     return dk, dv, dbias
 
 
-def sdpa_bwd_dq(q, k, v, dout, lse, d, *, bias=None, dq=None, **kw):
-    """dQ from the forward's stats and D.  Returns dq."""
+def sdpa_bwd_dq(q, k, v, dout, stats, *, bias=None, dq=None, **kw):
+    """dQ from the backward stats.  Returns dq."""
     group = kw.get("cu_seqlens_q") is not None
     p = make_problem(q, k, v, **kw)
     dq = _alloc_like(q, q.shape) if dq is None else dq
     _check(_lib.sdpa_bwd_dq(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
                             _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
-                            _ptr(dout), _strides(dout, group), _ptr(lse), _ptr(d),
+                            _ptr(dout), _strides(dout, group), _ptr(stats),
                             _ptr(dq), _strides(dq, group), _stream()))
     return dq

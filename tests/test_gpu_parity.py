@@ -228,8 +228,11 @@ def test_preprocess_matches_oracle_D(S):
     x = inputs.make_inputs(wl)
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "dout"))
     o, lse, _ = S.sdpa_fwd(q, k, v, causal=True)
-    d = S.sdpa_bwd_preprocess(o, do)
+    stats = S.sdpa_bwd_preprocess(o, do, lse)
     torch.cuda.synchronize()
+    n, off = S.stats_layout(2, 3, 333)
+    d = stats[:n].view(2, 3, 333)
+    assert torch.equal(stats[off:off + n].view(2, 3, 333), lse * np.float32(1.4426950408889634))
     # D of the kernel's own bf16 O, against the plain sum in fp64
     want = (o.double() * do.double()).sum(-1)
     assert torch.max(torch.abs(d.double() - want)).item() < 1e-3
@@ -239,6 +242,22 @@ def test_preprocess_matches_oracle_D(S):
     # rounding of O to the io type, sum_e dO_ie (O_gpu - O_ref)_ie
     dD = np.sum(x["dout"].double().numpy() * (_np(o) - ref["o"]), -1)
     assert np.max(np.abs(d.cpu().numpy() - ref["D"] - dD)) < 1e-3
+
+
+def test_split_backward_equals_sdpa_bwd(S):
+    # preprocess + dK/dV + dQ entry points give bitwise the results of sdpa_bwd
+    wl = inputs.small("f16", b=2, h=2, s_q=200, s_kv=260, bias=True, dropout_p=0.1, seed=31)
+    x = inputs.make_inputs(wl)
+    q, k, v, do, bias = (x[n].cuda() for n in ("q", "k", "v", "dout", "bias"))
+    kw = dict(causal=False, dropout_p=0.1, seed=5, offset=2)
+    o, lse, _ = S.sdpa_fwd(q, k, v, bias=bias, **kw)
+    dq, dk, dv, db = S.sdpa_bwd(q, k, v, o, do, lse, bias=bias, want_dbias=True, **kw)
+    stats = S.sdpa_bwd_preprocess(o, do, lse)
+    dk2, dv2, db2 = S.sdpa_bwd_dkdv(q, k, v, do, stats, bias=bias, want_dbias=True, **kw)
+    dq2 = S.sdpa_bwd_dq(q, k, v, do, stats, bias=bias, **kw)
+    torch.cuda.synchronize()
+    for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2), (db, db2)):
+        assert torch.equal(a_, b_)
 
 
 # ---------------------------------------------------- full-size workloads ---
