@@ -169,6 +169,14 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // direct-to-LDS loads) to complete; a barrier after it publishes the tile.
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Opaque copy: the compiler must assume the value changes here, so address
+// arithmetic built on it is redone at each use (one VALU op) instead of being
+// hoisted out of the loop into a register per use site.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // A operand from a tile stored as X[m][k] (k contiguous), rows permuted by
 // sig: lane gets X[mb + sig(l32)][kb + 8g + e].
 template <int D, typename T>
@@ -194,6 +202,63 @@ __device__ __forceinline__ u32x4 lds_trA(const T* buf, int kb, int mb, int lane)
   u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
+
+// Register-lean readers for the two A-operand patterns above.  For rows of
+// 64 or 128 elements the swizzled byte offset of every access a lane makes
+// is (per-lane base) XOR (compile-time constant) plus a compile-time row
+// offset: the XOR only touches bits below the row size and the per-lane
+// base's row part has those bits clear.  So a lane keeps one (rows) or two
+// (transposing) base registers, and each access costs one v_xor.  Other
+// widths use the general offset computation.
+template <int D, typename T> struct RowReader {
+  static constexpr bool FAST = (D == 64 || D == 128);
+  uint32_t pre;  // byte offset of (row sig(l32), chunk g), swizzled
+  int lane_;
+  __device__ __forceinline__ void init(int lane) {
+    lane_ = lane;
+    const int row = sig(lane & 31), g = lane >> 5;
+    pre = (uint32_t)(row * D * 2 + 16 * (g ^ Lds<D>::swz(row)));
+  }
+  // X[mb + sig(l32)][16 t + 8g + e]; mb a multiple of 32
+  __device__ __forceinline__ u32x4 read(const T* tile, int mb, int t) const {
+    if constexpr (FAST) {
+      const uint32_t off = (opaque(pre) ^ (uint32_t)(32 * t)) + (uint32_t)(mb * D * 2);
+      return *reinterpret_cast<const u32x4*>((const char*)tile + off);
+    } else {
+      return lds_rowA<D>(tile, mb, 16 * t, lane_);
+    }
+  }
+};
+
+template <int D, typename T> struct TrReader {
+  static constexpr bool FAST = (D == 64 || D == 128);
+  uint32_t pre[2];  // byte offsets of the two 4-row halves at kb = mb = 0
+  int lane_;
+  __device__ __forceinline__ void init(int lane) {
+    lane_ = lane;
+    const int i = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * (G >> 1) + 4 * h + (i >> 2);
+      const int col = 16 * (G & 1) + 4 * (i & 3);
+      pre[h] = (uint32_t)(2 * Lds<D>::off(row, col));
+    }
+  }
+  // X[kb + 8g + e][mb + l32], e = 0..7; kb a multiple of 16, mb of 32
+  __device__ __forceinline__ u32x4 read(const T* tile, int kb, int mb) const {
+    if constexpr (FAST) {
+      const char* base = (const char*)tile + kb * D * 2;
+      const uint32_t x = (uint32_t)(64 * (mb / 32));
+      const uint32_t o0 = opaque(pre[0]) ^ x, o1 = opaque(pre[1]) ^ x;
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o0));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o1));
+      u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    } else {
+      return lds_trA<D>(tile, kb, mb, lane_);
+    }
+  }
+};
 
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw; SC'11) -------------------
 struct Philox {

@@ -19,6 +19,10 @@
 // scale in its kernel arguments).
 #include "sdpa_kcommon.h"
 
+#ifndef SDPA_FWD_NBLK
+#define SDPA_FWD_NBLK 2
+#endif
+
 namespace sdpa {
 
 // workgroups per CU the register budget is sized for
@@ -28,7 +32,9 @@ template <int DQK, int DV, bool DROP> struct FwdOcc {
 
 template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(const FwdArgs a) {
-  constexpr int BR = 128, BC = 64;
+  constexpr int BR = 128;
+  constexpr int NBLK = SDPA_FWD_NBLK;  // 32-key blocks per key tile
+  constexpr int BC = 32 * NBLK;
   constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
   constexpr int DB = DV / 32;   // 32-wide blocks of d_v
   // Lazy rescaling: the running max is only raised (and O, l rescaled) when
@@ -87,22 +93,38 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;  // m_run in scaled log2 units
 
-  for (int it = 0; it < nt; ++it) {
+  RowReader<DQK, T> rdK;
+  TrReader<DV, T> rdV;
+  rdK.init(lane);
+  rdV.init(lane);
+
+  // One key tile: `cK`, `cV` hold tile `it`; the next tile is loaded into
+  // `nK`, `nV`.  Called with the two buffers swapped on alternate tiles so
+  // that every LDS address is a compile-time offset from a per-lane base.
+  auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV) __attribute__((always_inline)) {
     const int n0 = it * BC;
-    const T* cK = sK[it & 1];
-    const T* cV = sV[it & 1];
     wait_all();       // this wave's part of tile `it` has landed
     __syncthreads();  // ... and everyone's; tile it-1 is fully consumed
 
     // a wave whose rows see none of this tile skips it (causal)
     const bool active = !CAUSAL || n0 <= wq0 + 31;
 
-    // bias for this lane's row: 4 runs of 8 consecutive keys (issued before
+    // All K operands of this tile are requested first, so their LDS latency
+    // overlaps the prefetch issue and the rest of the requests.
+    u32x4 kop[NBLK * KT];
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = rdK.read(cK, 32 * blk, t);
+    }
+
+    // bias for this lane's row: runs of 8 consecutive keys (issued before
     // the next tile's prefetch so that waiting for them does not wait for it)
-    uint32_t braw[4][4];
+    uint32_t braw[2 * NBLK][4];
     if (BIAS && active) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 2 * NBLK; ++u) {
         int kb = n0 + 16 * u + 8 * g;  // u = 2*blk + hh
         const uint16_t* p = bg + (int64_t)row * a.sb_.s + kb;
         if (row_ok && kb + 8 <= skv && a.bias_vec) {
@@ -119,22 +141,21 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       }
     }
     if (it + 1 < nt) {
-      ldK.load(sK[(it + 1) & 1], n0 + BC, skv, w, lane);
-      ldV.load(sV[(it + 1) & 1], n0 + BC, skv, w, lane);
+      ldK.load(nK, n0 + BC, skv, w, lane);
+      ldV.load(nV, n0 + BC, skv, w, lane);
     }
-    if (!active) continue;
+    if (!active) return;
 
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // S^T = K Q^T for the tile's 32-key blocks
+    f32x16 s[NBLK];
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      u32x4 a0 = lds_rowA<DQK>(cK, 0, 16 * t, lane);
-      u32x4 a1 = lds_rowA<DQK>(cK, 32, 16 * t, lane);
-      s[0] = mfma32<T>(a0, qreg[t], s[0]);
-      s[1] = mfma32<T>(a1, qreg[t], s[1]);
-    }
+    for (int blk = 0; blk < NBLK; ++blk) s[blk] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) s[blk] = mfma32<T>(kop[NBLK * t + blk], qreg[t], s[blk]);
 
-    // keep bytes (dropout): 8 runs of 4 keys
+    // keep bytes (dropout): runs of 4 keys
     uint32_t kw[8];
     if (DROP) {
       uint32_t var4[8];
@@ -153,7 +174,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     float mrow;
     if (BIAS) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int u = 2 * blk + (r >> 3), e = r & 7;
@@ -162,13 +183,13 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
         }
       if (need_mask) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
       mrow = max_pair32(mx);
@@ -176,27 +197,35 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       const float hide = pos ? -INFINITY : INFINITY;
       if (need_mask) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : hide;
       }
       float mx = -INFINITY, mn = INFINITY;
       if (pos) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
         mx = max_pair32(mx);
         mrow = mx == -INFINITY ? -INFINITY : mx * c;
       } else {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mn = fminf(mn, s[blk][r]);
         mn = -max_pair32(-mn);
         mrow = mn == INFINITY ? -INFINITY : mn * c;
       }
     }
+
+    // all V^T operands of this tile, requested before the exponentials
+    u32x4 vop[2 * NBLK * DB];
+#pragma unroll
+    for (int tt = 0; tt < 2 * NBLK; ++tt)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vop[tt * DB + db] = rdV.read(cV, 16 * tt, 32 * db);
+
     const float m_new = fmaxf(m_run, mrow);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -205,27 +234,40 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       m_run = m_new;
     }
+    // Masked scores already hold -inf (scaled) / the hiding infinity (raw),
+    // so the exponent loop has no branches.  A zero scale is the one case
+    // where c * (+-inf) is not -inf; it is fixed up after the loop.
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[blk][r] = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
+                         : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_run));
+    if (!BIAS && need_mask && c == 0.f) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : 0.f;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
-                        : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_run));
-        if (!BIAS && need_mask) pv = visible(blk, r) ? pv : 0.f;
-        psum += pv;
-        if (DROP) {
+      for (int r = 0; r < 16; ++r) psum += s[blk][r];
+    l_run += psum;
+    if (DROP) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
           bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
-          pv = keep ? pv : 0.f;
+          s[blk][r] = keep ? s[blk][r] : 0.f;
         }
-        s[blk][r] = pv;
-      }
     }
-    l_run += psum;
-    u32x4 pb[4];
+    u32x4 pb[2 * NBLK];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2 * NBLK; ++tt) {
       int blk = tt >> 1, r0 = 8 * (tt & 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
@@ -234,7 +276,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     if (DROP && a.keep && row_ok) {
       uint8_t* kp = a.keep + (((int64_t)b * a.H + h) * a.seq.s_q + row) * a.seq.s_kv;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4 * NBLK; ++k) {
         int kv0 = n0 + 16 * (k >> 1) + 8 * g + 4 * (k & 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -247,13 +289,15 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2 * NBLK; ++tt) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        u32x4 av = lds_trA<DV>(cV, 16 * tt, 32 * db, lane);
-        oacc[db] = mfma32<T>(av, pb[tt], oacc[db]);
-      }
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb[tt], oacc[db]);
     }
+  };
+
+  for (int it = 0; it < nt; it += 2) {
+    tile(it, sK[0], sV[0], sK[1], sV[1]);
+    if (it + 1 < nt) tile(it + 1, sK[1], sV[1], sK[0], sV[0]);
   }
 
   // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2
