@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sdpa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -33,6 +35,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F, int I = 0> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
 
 __device__ __forceinline__ int sig(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -169,13 +179,25 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // direct-to-LDS loads) to complete; a barrier after it publishes the tile.
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Opaque copy: the compiler must assume the value changes here, so address
-// arithmetic built on it is redone at each use (one VALU op) instead of being
-// hoisted out of the loop into a register per use site.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
+// v ^ K as one v_xor_b32 that the compiler can neither hoist out of a loop
+// nor merge with another: LDS offsets formed this way are recomputed at
+// each use (one VALU op) instead of each holding a register for the whole
+// loop.  K == 0 is v itself.
+template <uint32_t K> __device__ __forceinline__ uint32_t xor_at_use(uint32_t v) {
+  if constexpr (K == 0) {
+    return v;
+  } else {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(K), "v"(v));
+    return r;
+  }
 }
+
+// An empty side-effecting statement.  Placed inside a wave-uniform `if`, it
+// keeps the compiler from if-converting the block into unconditional
+// per-element selects (which it otherwise does for cheap-looking bodies):
+// the branch stays a scalar branch and the skipped work costs nothing.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
 // A operand from a tile stored as X[m][k] (k contiguous), rows permuted by
 // sig: lane gets X[mb + sig(l32)][kb + 8g + e].
@@ -208,8 +230,10 @@ __device__ __forceinline__ u32x4 lds_trA(const T* buf, int kb, int mb, int lane)
 // is (per-lane base) XOR (compile-time constant) plus a compile-time row
 // offset: the XOR only touches bits below the row size and the per-lane
 // base's row part has those bits clear.  So a lane keeps one (rows) or two
-// (transposing) base registers, and each access costs one v_xor.  Other
-// widths use the general offset computation.
+// (transposing) base registers, and each access costs at most one v_xor.
+// Other widths use the general offset computation.
+// refresh() is called once per loop trip: the XORed offsets are then formed
+// once per trip (shared by every row block) and die within it.
 template <int D, typename T> struct RowReader {
   static constexpr bool FAST = (D == 64 || D == 128);
   uint32_t pre;  // byte offset of (row sig(l32), chunk g), swizzled
@@ -220,12 +244,13 @@ template <int D, typename T> struct RowReader {
     pre = (uint32_t)(row * D * 2 + 16 * (g ^ Lds<D>::swz(row)));
   }
   // X[mb + sig(l32)][16 t + 8g + e]; mb a multiple of 32
-  __device__ __forceinline__ u32x4 read(const T* tile, int mb, int t) const {
+  template <int T_>
+  __device__ __forceinline__ u32x4 read(const T* tile, int mb) const {
     if constexpr (FAST) {
-      const uint32_t off = (opaque(pre) ^ (uint32_t)(32 * t)) + (uint32_t)(mb * D * 2);
+      const uint32_t off = xor_at_use<32u * T_>(pre) + (uint32_t)(mb * D * 2);
       return *reinterpret_cast<const u32x4*>((const char*)tile + off);
     } else {
-      return lds_rowA<D>(tile, mb, 16 * t, lane_);
+      return lds_rowA<D>(tile, mb, 16 * T_, lane_);
     }
   }
 };
@@ -244,18 +269,19 @@ template <int D, typename T> struct TrReader {
       pre[h] = (uint32_t)(2 * Lds<D>::off(row, col));
     }
   }
-  // X[kb + 8g + e][mb + l32], e = 0..7; kb a multiple of 16, mb of 32
-  __device__ __forceinline__ u32x4 read(const T* tile, int kb, int mb) const {
+  // X[kb + 8g + e][MB + l32], e = 0..7; kb a multiple of 16, MB of 32
+  template <int MB>
+  __device__ __forceinline__ u32x4 read(const T* tile, int kb) const {
     if constexpr (FAST) {
       const char* base = (const char*)tile + kb * D * 2;
-      const uint32_t x = (uint32_t)(64 * (mb / 32));
-      const uint32_t o0 = opaque(pre[0]) ^ x, o1 = opaque(pre[1]) ^ x;
+      constexpr uint32_t x = (uint32_t)(64 * (MB / 32));
+      const uint32_t o0 = xor_at_use<x>(pre[0]), o1 = xor_at_use<x>(pre[1]);
       s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o0));
       s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o1));
       u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
       return u32x4{l2[0], l2[1], h2[0], h2[1]};
     } else {
-      return lds_trA<D>(tile, kb, mb, lane_);
+      return lds_trA<D>(tile, kb, MB, lane_);
     }
   }
 };

@@ -113,10 +113,10 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     // overlaps the prefetch issue and the rest of the requests.
     u32x4 kop[NBLK * KT];
     if (active) {
+      static_for<KT>([&](auto t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = rdK.read(cK, 32 * blk, t);
+        for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = rdK.template read<t>(cK, 32 * blk);
+      });
     }
 
     // bias for this lane's row: runs of 8 consecutive keys (issued before
@@ -167,6 +167,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     // Scores in scaled log2 units.  Without bias the scale is folded into
     // the exponent's FMA and the row max is taken on the raw scores.
     const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > wq0);
+    // element (blk, r) holds key n0 + 8g + koff(blk, r); it is visible iff
+    // koff <= lim (key < s_kv and, causal, key <= row)
     auto visible = [&](int blk, int r) {
       int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
       return kv < skv && (!CAUSAL || kv <= row);
@@ -182,6 +184,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
           s[blk][r] = __builtin_fmaf(s[blk][r], c, to_f32<T>((uint16_t)bits) * kLog2e);
         }
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
@@ -196,6 +199,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     } else {
       const float hide = pos ? -INFINITY : INFINITY;
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
@@ -223,11 +227,13 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     u32x4 vop[2 * NBLK * DB];
 #pragma unroll
     for (int tt = 0; tt < 2 * NBLK; ++tt)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vop[tt * DB + db] = rdV.read(cV, 16 * tt, 32 * db);
+      static_for<DB>([&](auto db) __attribute__((always_inline)) {
+        vop[tt * DB + db] = rdV.template read<32 * db>(cV, 16 * tt);
+      });
 
     const float m_new = fmaxf(m_run, mrow);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
+      keep_branch();
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -244,6 +250,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
         s[blk][r] = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
                          : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_run));
     if (!BIAS && need_mask && c == 0.f) {
+      keep_branch();
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
