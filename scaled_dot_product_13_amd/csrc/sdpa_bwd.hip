@@ -420,10 +420,19 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     ldK.load(sK[0], 0, skv, w, lane);
     ldV.load(sV[0], 0, skv, w, lane);
   }
-  for (int it = 0; it < nt; ++it) {
+  RowReader<DQK, T> rdK;
+  RowReader<DV, T> rdV;
+  TrReader<DQK, T> rdKt;
+  rdK.init(lane);
+  rdV.init(lane);
+  rdKt.init(lane);
+  const float c = a.scale_log2;
+
+  // One key tile: `cK`, `cV` hold tile `it`, the next one is loaded into
+  // `nK`, `nV`; alternate tiles swap the buffers so that LDS addresses are
+  // compile-time offsets from per-lane bases.
+  auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV) __attribute__((always_inline)) {
     const int n0 = it * BC;
-    const T* cK = sK[it & 1];
-    const T* cV = sV[it & 1];
     wait_all();
     __syncthreads();
     const bool active = !CAUSAL || (n0 <= q0 + 32 * w + 31);
@@ -447,28 +456,24 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
         }
       }
     }
-
     if (it + 1 < nt) {
-      ldK.load(sK[(it + 1) & 1], n0 + BC, skv, w, lane);
-      ldV.load(sV[(it + 1) & 1], n0 + BC, skv, w, lane);
+      ldK.load(nK, n0 + BC, skv, w, lane);
+      ldV.load(nV, n0 + BC, skv, w, lane);
     }
-    if (!active) continue;
+    if (!active) return;
 
+    // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      u32x4 a0 = lds_rowA<DQK>(cK, 0, 16 * t, lane);
-      u32x4 a1 = lds_rowA<DQK>(cK, 32, 16 * t, lane);
+    static_for<KT>([&](auto t) __attribute__((always_inline)) {
+      const u32x4 a0 = rdK.template read<t>(cK, 0), a1 = rdK.template read<t>(cK, 32);
       s[0] = mfma32<T>(a0, qreg[t], s[0]);
       s[1] = mfma32<T>(a1, qreg[t], s[1]);
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      u32x4 a0 = lds_rowA<DV>(cV, 0, 16 * t, lane);
-      u32x4 a1 = lds_rowA<DV>(cV, 32, 16 * t, lane);
+    });
+    static_for<VT>([&](auto t) __attribute__((always_inline)) {
+      const u32x4 a0 = rdV.template read<t>(cV, 0), a1 = rdV.template read<t>(cV, 32);
       dp[0] = mfma32<T>(a0, doreg[t], dp[0]);
       dp[1] = mfma32<T>(a1, doreg[t], dp[1]);
-    }
+    });
 
     uint32_t kw[8];
     if (DROP) {
@@ -478,47 +483,66 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
       quad_keep_words<true>(var4, (uint32_t)row >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
     }
 
-    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
-    u32x4 dsb[4];
+    // P^T = exp2(scale log2e S^T (+ log2e bias) - LSE log2e).  Rows past s_q
+    // have Q = dO = 0 and LSE = D = 0, so their dS is exactly 0 without a
+    // mask; keys past s_kv or above the diagonal are zeroed on the tiles
+    // that have them.
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[blk][r] * a.scale_log2 - lse2;
+        float x;
         if (BIAS) {
-          int u = 2 * blk + (r >> 3), e = r & 7;
-          uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          x += to_f32<T>((uint16_t)bits) * kLog2e;
+          const int u = 2 * blk + (r >> 3), e = r & 7;
+          const uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          x = __builtin_fmaf(s[blk][r], c, __builtin_fmaf(to_f32<T>((uint16_t)bits), kLog2e, -lse2));
+        } else {
+          x = __builtin_fmaf(s[blk][r], c, -lse2);
         }
-        float p = __builtin_amdgcn_exp2f(x);
-        if (need_mask || !row_ok) {
-          int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-          bool vis = row_ok && kv < skv && (!CAUSAL || kv <= row);
-          p = vis ? p : 0.f;
+        s[blk][r] = __builtin_amdgcn_exp2f(x);
+      }
+    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
+    if (need_mask) {
+      keep_branch();
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+          const bool vis = kv < skv && (!CAUSAL || kv <= row);
+          s[blk][r] = vis ? s[blk][r] : 0.f;
         }
-        float z = 1.f;
+    }
+    // dS^T = P^T o (dP^T o Z - D), packed as the B operand of dQ^T += K^T dS^T
+    u32x4 dsb[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int blk = tt >> 1, r0 = 8 * (tt & 1);
+      float ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        float dpz = dp[blk][r];
         if (DROP) {
-          int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
-          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
-          z = keep ? rescale : 0.f;
+          const int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
+          const bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          dpz = keep ? dpz * rescale : 0.f;
         }
-        s[blk][r] = p * (dp[blk][r] * z - Drow);
+        ds[e] = s[blk][r] * (dpz - Drow);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsb[tt][e] = pack2<T>(ds[2 * e], ds[2 * e + 1]);
     }
+    static_for<QB>([&](auto qb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      int blk = tt >> 1, r0 = 8 * (tt & 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dsb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        u32x4 ak = lds_trA<DQK>(cK, 16 * tt, 32 * qb, lane);
-        dqacc[qb] = mfma32<T>(ak, dsb[tt], dqacc[qb]);
-      }
-    }
+      for (int tt = 0; tt < 4; ++tt)
+        dqacc[qb] = mfma32<T>(rdKt.template read<32 * qb>(cK, 16 * tt), dsb[tt], dqacc[qb]);
+    });
+  };
+
+  for (int it = 0; it < nt; it += 2) {
+    tile(it, sK[0], sV[0], sK[1], sV[1]);
+    if (it + 1 < nt) tile(it + 1, sK[1], sV[1], sK[0], sV[0]);
   }
 
   if (row_ok) {
