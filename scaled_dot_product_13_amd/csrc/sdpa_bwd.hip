@@ -71,31 +71,38 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV (and dBias).  Workgroup = 4 waves x 32 keys; query tiles of 64.
-// Per wave and query tile, with the queries fetched in sig order:
-//   S  = Q K^T   (A = Q rows from LDS, B = K^T in registers)
-//   dP = dO V^T  (A = dO rows from LDS, B = V^T in registers)
-// The accumulators hold one key per lane, so P and dS feed
-//   dV^T += dO^T (P o Z)   and   dK^T += Q^T dS
-// directly as B operands; the A operands dO^T and Q^T come from the same LDS
-// tiles through the transposing LDS read.
+// dK, dV (and dBias).  Workgroup = 128 keys, 8 waves in two roles; wave
+// kb = w & 3 owns keys kv0 + 32 kb + l32 (one key per lane) in both roles.
+// Query tiles of 32 rows stream through LDS; per tile, with the queries
+// fetched in sig order:
+//   role A (w < 4):  S = Q K^T (B = K^T in registers), P = exp2(c S - LSE'),
+//                    dV^T += dO^T (P o Z)   (A = dO^T by transposing read)
+//                    and P is handed to role B through LDS;
+//   role B (w >= 4), one tile behind:
+//                    dP = dO V^T (B = V^T in registers),
+//                    dS = P o (dP o Z - D), dBias = dS,
+//                    dK^T += Q^T dS          (A = Q^T by transposing read).
+// The two waves of a key block share a SIMD, so one's exponentials and
+// element-wise work overlap the other's matrix products, and each role keeps
+// only half of the stationary state (K and dV, or V and dK) in registers.
 template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
-__global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
-  constexpr int BC = 128, BQ = 32, QBLK = BQ / 32;
+__global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
+  constexpr int BC = 128, BQ = 32, NSET = 3;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
-  // Query tiles are triple-buffered: while tile i is consumed (elementwise
-  // step, dV and dK products) the S and dP products of tile i+1 are issued
-  // and tile i+2 is loading.  The bias tile joins them through LDS when it
-  // fits (d_qk <= 128).
-  constexpr int NB = 3;
   constexpr bool BIAS_LDS = BIAS && DQK <= 128;
-  __shared__ __attribute__((aligned(1024))) T sQ[NB][BQ * DQK];
-  __shared__ __attribute__((aligned(1024))) T sO[NB][BQ * DV];
-  __shared__ __attribute__((aligned(1024))) T sB[BIAS_LDS ? NB : 1][BIAS_LDS ? BQ * BC : 64];
-  __shared__ __attribute__((aligned(256))) float sL[NB][BQ], sD[NB][BQ];
+  // Query-side tiles are triple-buffered: role A reads set i % 3, role B
+  // set (i - 1) % 3 and set (i + 1) % 3 is loading.
+  __shared__ __attribute__((aligned(1024))) T sQ[NSET][BQ * DQK];
+  __shared__ __attribute__((aligned(1024))) T sO[NSET][BQ * DV];
+  __shared__ __attribute__((aligned(1024))) T sB[BIAS_LDS ? NSET : 1][BIAS_LDS ? BQ * BC : 64];
+  __shared__ __attribute__((aligned(256))) float sL[NSET][BQ], sD[NSET][BQ];
+  // P from role A to role B: [slot][key block][4 groups of 4 elements][lane]
+  __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
+  const int kb = w & 3;
+  const bool roleA = w < 4;
   const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H, a.B);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
@@ -116,58 +123,46 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
     if (a.dbias) dbg = (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
   }
 
-  const int wk0 = kv0 + 32 * w;        // this wave's first key
-  const int kvr = wk0 + l32;           // this lane's key
+  const int wk0 = kv0 + 32 * kb;  // this wave's first key
+  const int kvr = wk0 + l32;      // this lane's key
   const bool kv_ok = kvr < skv;
-  u32x4 kreg[KT], vreg[VT];
-#pragma unroll
-  for (int t = 0; t < KT; ++t)
-    kreg[t] = kv_ok ? *(const u32x4*)(kg + (int64_t)kvr * a.sk_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int t = 0; t < VT; ++t)
-    vreg[t] = kv_ok ? *(const u32x4*)(vg + (int64_t)kvr * a.sv_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
-
   DropKey dk{};
   const uint32_t bh = (uint32_t)(b * a.H + h);
   if (DROP) dk = drop_key(a.drop);
   const float rescale = DROP ? a.drop.rescale : 1.f;
   const float c = a.scale_log2;
 
-  f32x16 dkacc[QB], dvacc[VB];
-#pragma unroll
-  for (int i = 0; i < QB; ++i) dkacc[i] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < VB; ++i) dvacc[i] = f32x16{};
-
   // causal: query rows below kv0 see none of these keys
   const int q_begin = CAUSAL ? (kv0 / BQ) * BQ : 0;
   const int nq = sq > q_begin ? (sq - q_begin + BQ - 1) / BQ : 0;
-  if (CAUSAL && dbg && kv_ok) {
+  if (CAUSAL && dbg && !roleA && kv_ok) {
     // dBias is zero wherever the mask hides the key: rows [0, q_begin)
     for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
   }
 
-  // bias tiles come through LDS when the whole 64 x 128 tile is in range and
+  // bias tiles come through LDS when the whole 32 x 128 tile is in range and
   // its rows are 16-byte aligned; otherwise each lane reads its elements.
   const bool bias_lds = BIAS_LDS && a.bias_vec && kv0 + BC <= skv;
-  TileLoader<DQK, BQ, T> ldQ;
-  TileLoader<DV, BQ, T> ldO;
-  TileLoader<BC, BQ, T> ldB;
-  ldQ.init(qg, a.sq_.s, w, lane);
-  ldO.init(dog, a.sdo_.s, w, lane);
+  constexpr int NWQ = (BQ * DQK / 8) % 512 == 0 ? 8 : 4;
+  constexpr int NWO = (BQ * DV / 8) % 512 == 0 ? 8 : 4;
+  TileLoader<DQK, BQ, T, NWQ> ldQ;
+  TileLoader<DV, BQ, T, NWO> ldO;
+  TileLoader<BC, BQ, T, 8> ldB;
+  if (w < NWQ) ldQ.init(qg, a.sq_.s, w, lane);
+  if (w < NWO) ldO.init(dog, a.sdo_.s, w, lane);
   if (BIAS_LDS && bias_lds) ldB.init((const T*)(bg + kv0), a.sb_.s, w, lane);
   auto issue = [&](int i) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ, buf = i % NB;
-    ldQ.load(sQ[buf], q0, sq, w, lane);
-    ldO.load(sO[buf], q0, sq, w, lane);
-    if (BIAS_LDS && bias_lds) ldB.load(sB[buf], q0, sq, w, lane);
-    // the 64 LSE*log2(e) (wave 0) and D (wave 1) values, one row per lane,
+    const int q0 = q_begin + i * BQ, set = i % NSET;
+    if (w < NWQ) ldQ.load(sQ[set], q0, sq, w, lane);
+    if (w < NWO) ldO.load(sO[set], q0, sq, w, lane);
+    if (BIAS_LDS && bias_lds) ldB.load(sB[set], q0, sq, w, lane);
+    // the 32 LSE*log2(e) (wave 6) and D (wave 7) values, one row per lane,
     // rows clamped to the sequence
-    if (w < 2 && lane < BQ) {
+    if (w >= 6 && lane < BQ) {
       int r = q0 + lane;
       r = r < sq ? r : sq - 1;
-      const float* src = (w == 0 ? a.lse2 : a.dvec) + st_base + r;
-      float* dst = w == 0 ? sL[buf] : sD[buf];
+      const float* src = (w == 6 ? a.lse2 : a.dvec) + st_base + r;
+      float* dst = w == 6 ? sL[set] : sD[set];
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
@@ -180,172 +175,205 @@ __global__ void __launch_bounds__(256, 1) dkdv_mfma(const BwdArgs a) {
     return (q0 + BQ > sq) || (wk0 + 31 >= skv) || (CAUSAL && q0 < wk0 + 31);
   };
 
-  // S = Q K^T and dP = dO V^T of tile i (queries in sig order)
-  auto products = [&](int i, f32x16* s, f32x16* dp) __attribute__((always_inline)) {
-    const T* cQ = sQ[i % NB];
-    const T* cO = sO[i % NB];
-#pragma unroll
-    for (int qb = 0; qb < QBLK; ++qb) s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int qb = 0; qb < QBLK; ++qb)
-        s[qb] = mfma32<T>(lds_rowA<DQK>(cQ, 32 * qb, 16 * t, lane), kreg[t], s[qb]);
-#pragma unroll
-    for (int t = 0; t < VT; ++t)
-#pragma unroll
-      for (int qb = 0; qb < QBLK; ++qb)
-        dp[qb] = mfma32<T>(lds_rowA<DV>(cO, 32 * qb, 16 * t, lane), vreg[t], dp[qb]);
-  };
+  RowReader<DQK, T> rdQ;
+  TrReader<DV, T> rdOt;
+  RowReader<DV, T> rdO;
+  TrReader<DQK, T> rdQt;
+  rdQ.init(lane);
+  rdOt.init(lane);
+  rdO.init(lane);
+  rdQt.init(lane);
+  // this lane's P slot: 4 x 16 bytes at stride 1 KiB
+  const uint32_t p_lane = lds_addr(&sP[0][kb][0][0]) + 16 * lane;
+  constexpr uint32_t P_SLOT = 4 * 4 * 64 * 16;
 
-  // elementwise step of tile i: P (dropped out) and dS into B-operand form
-  auto elementwise = [&](bool need_mask, int i, const f32x16* s, const f32x16* dp, u32x4* pb,
-                         u32x4* dsb) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ, buf = i % NB;
-    const float* cL = sL[buf];
-    const float* cD = sD[buf];
-    const T* cB = sB[BIAS_LDS ? buf : 0];
+  // ---- role A: S, P, dV for tile i -----------------------------------------
+  auto stepA = [&](int i, const u32x4* reg, f32x16* acc) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ, set = i % NSET;
+    const auto vQ = rdQ.view(sQ[set]);
+    const auto vOt = rdOt.view(sO[set]);
+    f32x16 s = f32x16{};
+    static_for<KT>([&](auto t) __attribute__((always_inline)) {
+      s = mfma32<T>(vQ.template read<t>(0), reg[t], s);
+    });
     uint32_t kw[8];
     if (DROP) {
-      // 4x4 patches along this lane's queries: 8 per 64 rows (the second
-      // half unused when the tile has 32 rows)
+      // 4x4 patches along this lane's queries (the first 4 of the 8 used)
       uint32_t var4[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
       quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
     }
+    const float* cL = sL[set];
+    const T* cB = sB[BIAS_LDS ? set : 0];
+    float pv[16];
 #pragma unroll
-    for (int qb = 0; qb < QBLK; ++qb) {
+    for (int hh = 0; hh < 2; ++hh) {
+      const int lb = 16 * hh + 8 * g;  // first of my 8 consecutive rows
+      const f32x4 L0 = *(const f32x4*)(cL + lb), L1 = *(const f32x4*)(cL + lb + 4);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int lb = 32 * qb + 16 * hh + 8 * g;  // first of my 8 consecutive rows
-        const f32x4 L0 = *(const f32x4*)(cL + lb), L1 = *(const f32x4*)(cL + lb + 4);
-        const f32x4 D0 = *(const f32x4*)(cD + lb), D1 = *(const f32x4*)(cD + lb + 4);
-        float pv[8], dv_[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * hh + e;
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * hh + e;
+        float x = -(e < 4 ? L0[e] : L1[e - 4]);  // exponent = c s + log2e bias - LSE log2e
+        if (BIAS) {
           const int ql = lb + e, qr = q0 + ql;
-          const float L = e < 4 ? L0[e] : L1[e - 4];
-          const float Dq = e < 4 ? D0[e] : D1[e - 4];
-          float off = -L;  // exponent = scale*log2e*s + log2e*bias - LSE*log2e
-          if (BIAS) {
-            float bval = 0.f;
-            if (bias_lds)
-              bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * w + l32)));
-            else if (kv_ok && qr < sq)
-              bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
-            off = __builtin_fmaf(bval, kLog2e, off);
-          }
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, off));
-          if (need_mask) {
-            const bool vis = qr < sq && kv_ok && (!CAUSAL || kvr <= qr);
-            p = vis ? p : 0.f;
-          }
-          float z = 1.f, pz = p;
-          if (DROP) {
-            const int k = 4 * qb + 2 * hh + (e >> 2);
-            const bool keep = ((kw[k] >> (8 * (e & 3))) & 0xffu) >= dk.thr;
-            z = keep ? rescale : 0.f;
-            pz = keep ? p : 0.f;
-          }
-          const float ds = p * (dp[qb][r] * z - Dq);
-          if (BIAS && dbg && kv_ok && qr < sq)
-            dbg[(int64_t)qr * a.sdb_.s + kvr] = (uint16_t)(pack2<T>(ds, 0.f) & 0xffffu);
-          pv[e] = pz;
-          dv_[e] = ds;
+          float bval = 0.f;
+          if (bias_lds)
+            bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * kb + l32)));
+          else if (kv_ok && qr < sq)
+            bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
+          x = __builtin_fmaf(bval, kLog2e, x);
         }
-        const int tt = 2 * qb + hh;
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, x));
+      }
+    }
+    if (tile_needs_mask(i)) {
+      keep_branch();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = q0 + 16 * (r >> 3) + 8 * g + (r & 7);
+        const bool vis = qr < sq && kv_ok && (!CAUSAL || kvr <= qr);
+        pv[r] = vis ? pv[r] : 0.f;
+      }
+    }
+    // hand P to role B: dropped elements carry the sign bit
+    u32x4 pb[2];
+    {
+      uint32_t bits[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bits[r] = __float_as_uint(pv[r]);
+        if (DROP) {
+          const int k = 2 * (r >> 3) + ((r & 7) >> 2);
+          const bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          bits[r] |= keep ? 0u : 0x80000000u;
+        }
+      }
+      const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(pa + 1024 * j) =
+            u32x4{bits[4 * j], bits[4 * j + 1], bits[4 * j + 2], bits[4 * j + 3]};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[tt][e] = pack2<T>(pv[2 * e], pv[2 * e + 1]);
-          dsb[tt][e] = pack2<T>(dv_[2 * e], dv_[2 * e + 1]);
+          const int r = 8 * tt + 2 * e;
+          const float p0 = DROP ? ((bits[r] >> 31) ? 0.f : pv[r]) : pv[r];
+          const float p1 = DROP ? ((bits[r + 1] >> 31) ? 0.f : pv[r + 1]) : pv[r + 1];
+          pb[tt][e] = pack2<T>(p0, p1);
+        }
+    }
+    // dV^T += dO^T (P o Z)
+    static_for<VB>([&](auto vb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[vb] = mfma32<T>(vOt.template read<32 * vb>(16 * tt), pb[tt], acc[vb]);
+    });
+  };
+
+  // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
+  auto stepB = [&](int i, const u32x4* reg, f32x16* acc) __attribute__((always_inline)) {
+    const int q0 = q_begin + i * BQ, set = i % NSET;
+    const auto vO = rdO.view(sO[set]);
+    const auto vQt = rdQt.view(sQ[set]);
+    f32x16 dp = f32x16{};
+    static_for<VT>([&](auto t) __attribute__((always_inline)) {
+      dp = mfma32<T>(vO.template read<t>(0), reg[t], dp);
+    });
+    const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
+    u32x4 pw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = lds_load16(pa + 1024 * j);
+    const float* cD = sD[set];
+    u32x4 dsb[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int lb = 16 * hh + 8 * g;
+      const f32x4 D0 = *(const f32x4*)(cD + lb), D1 = *(const f32x4*)(cD + lb + 4);
+      float ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * hh + e;
+        const uint32_t bits = pw[r >> 2][r & 3];
+        const float Dq = e < 4 ? D0[e] : D1[e - 4];
+        float p, dpz;
+        if (DROP) {
+          p = __uint_as_float(bits & 0x7fffffffu);
+          dpz = (bits >> 31) ? 0.f : dp[r] * rescale;
+        } else {
+          p = __uint_as_float(bits);
+          dpz = dp[r];
+        }
+        ds[e] = p * (dpz - Dq);
+        if (BIAS && dbg && kv_ok) {
+          const int qr = q0 + lb + e;
+          if (qr < sq) dbg[(int64_t)qr * a.sdb_.s + kvr] = (uint16_t)(pack2<T>(ds[e], 0.f) & 0xffffu);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsb[hh][e] = pack2<T>(ds[2 * e], ds[2 * e + 1]);
+    }
+    // dK^T += Q^T dS
+    static_for<QB>([&](auto qb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[qb] = mfma32<T>(vQt.template read<32 * qb>(16 * tt), dsb[tt], acc[qb]);
+    });
+  };
+
+  if (nq > 0) issue(0);
+  // Each role runs its own copy of the trip loop, so its stationary operands
+  // and accumulators are sized for it alone; both copies meet the same
+  // barriers.  Trip i: role A takes tile i, role B tile i - 1.
+  auto run = [&](auto is_a) __attribute__((always_inline)) {
+    constexpr bool IS_A = decltype(is_a)::value;
+    constexpr int NR = IS_A ? KT : VT, NA = IS_A ? VB : QB;
+    u32x4 reg[NR];  // K^T (role A) or V^T (role B) as B operands
+    {
+      const T* src = IS_A ? kg + (int64_t)kvr * a.sk_.s : vg + (int64_t)kvr * a.sv_.s;
+#pragma unroll
+      for (int t = 0; t < NR; ++t)
+        reg[t] = kv_ok ? *(const u32x4*)(src + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+    }
+    f32x16 acc[NA];  // dV^T (role A) or dK^T (role B), one key per lane
+#pragma unroll
+    for (int j = 0; j < NA; ++j) acc[j] = f32x16{};
+
+    for (int i = 0; i <= nq; ++i) {
+      wait_all();
+      __syncthreads();  // tile i landed; P(i-1) written; set (i+1)%3 free
+      if (i + 1 < nq) issue(i + 1);
+      if constexpr (IS_A) {
+        if (i < nq && tile_active(i)) stepA(i, reg, acc);
+      } else if (i >= 1) {
+        if (tile_active(i - 1)) {
+          stepB(i - 1, reg, acc);
+        } else if (CAUSAL && dbg && kv_ok) {
+          const int q0 = q_begin + (i - 1) * BQ;  // the whole tile is hidden from my key
+          for (int r = q0 + g; r < min(q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+        }
+      }
+    }
+
+    // epilogue: dV = rescale * dV^T acc (role A), dK = scale * dK^T acc (role B)
+    if (kv_ok) {
+      T* dst = IS_A ? base_ptr_mut<T>(a.dv, a.sdv_, sp, h, false) + (int64_t)kvr * a.sdv_.s
+                    : base_ptr_mut<T>(a.dk, a.sdk_, sp, h, false) + (int64_t)kvr * a.sdk_.s;
+      const float f = IS_A ? rescale : a.scale;
+#pragma unroll
+      for (int db = 0; db < NA; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          int d = 32 * db + 8 * rr + 4 * g;
+          u32x2 v2;
+          v2[0] = pack2<T>(acc[db][4 * rr] * f, acc[db][4 * rr + 1] * f);
+          v2[1] = pack2<T>(acc[db][4 * rr + 2] * f, acc[db][4 * rr + 3] * f);
+          *(u32x2*)(dst + d) = v2;
         }
       }
     }
   };
-  // dV^T += dO^T (P o Z) and dK^T += Q^T dS for tile i
-  auto dvdk = [&](int i, const u32x4* pb, const u32x4* dsb) __attribute__((always_inline)) {
-    const T* cQ = sQ[i % NB];
-    const T* cO = sO[i % NB];
-#pragma unroll
-    for (int tt = 0; tt < 2 * QBLK; ++tt) {
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-        dvacc[vb] = mfma32<T>(lds_trA<DV>(cO, 16 * tt, 32 * vb, lane), pb[tt], dvacc[vb]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        dkacc[qb] = mfma32<T>(lds_trA<DQK>(cQ, 16 * tt, 32 * qb, lane), dsb[tt], dkacc[qb]);
-    }
-  };
-  // One pipelined step: the products of tile i+1 are issued before the
-  // elementwise work and the dV / dK products of tile i, so the matrix cores
-  // have independent work while the vector unit runs.
-  auto run = [&](int i, const f32x16* cs, const f32x16* cdp, f32x16* ns, f32x16* ndp)
-      __attribute__((always_inline)) {
-    if (i + 1 < nq && tile_active(i + 1)) products(i + 1, ns, ndp);
-    if (tile_active(i)) {
-      u32x4 pb[2 * QBLK], dsb[2 * QBLK];
-      elementwise(tile_needs_mask(i), i, cs, cdp, pb, dsb);
-      dvdk(i, pb, dsb);
-    } else {
-      const int q0 = q_begin + i * BQ;  // the whole tile is hidden from my key
-      if (CAUSAL && dbg && kv_ok)
-        for (int r = q0 + g; r < min(q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
-    }
-  };
-
-  if (nq > 0) {
-    issue(0);
-    if (nq > 1) issue(1);
-    wait_all();
-    __syncthreads();
-    f32x16 sA[QBLK], dA[QBLK], sB_[QBLK], dB_[QBLK];
-    if (tile_active(0)) products(0, sA, dA);
-    // two iterations per trip so that the current / next accumulators swap
-    // roles without register copies
-    for (int i = 0; i < nq; i += 2) {
-      if (i > 0) {
-        wait_all();
-        __syncthreads();
-      }
-      if (i + 2 < nq) issue(i + 2);
-      run(i, sA, dA, sB_, dB_);
-      if (i + 1 >= nq) break;
-      wait_all();
-      __syncthreads();
-      if (i + 3 < nq) issue(i + 3);
-      run(i + 1, sB_, dB_, sA, dA);
-    }
-  }
-
-  // epilogue: dK = scale * dK^T acc, dV = rescale * dV^T acc (one key per lane)
-  if (kv_ok) {
-    T* dkr = base_ptr_mut<T>(a.dk, a.sdk_, sp, h, false) + (int64_t)kvr * a.sdk_.s;
-    T* dvr = base_ptr_mut<T>(a.dv, a.sdv_, sp, h, false) + (int64_t)kvr * a.sdv_.s;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        int d = 32 * qb + 8 * rr + 4 * g;
-        u32x2 v2;
-        v2[0] = pack2<T>(dkacc[qb][4 * rr] * a.scale, dkacc[qb][4 * rr + 1] * a.scale);
-        v2[1] = pack2<T>(dkacc[qb][4 * rr + 2] * a.scale, dkacc[qb][4 * rr + 3] * a.scale);
-        *(u32x2*)(dkr + d) = v2;
-      }
-    }
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        int d = 32 * vb + 8 * rr + 4 * g;
-        u32x2 v2;
-        v2[0] = pack2<T>(dvacc[vb][4 * rr] * rescale, dvacc[vb][4 * rr + 1] * rescale);
-        v2[1] = pack2<T>(dvacc[vb][4 * rr + 2] * rescale, dvacc[vb][4 * rr + 3] * rescale);
-        *(u32x2*)(dvr + d) = v2;
-      }
-    }
-  }
+  if (roleA) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -708,7 +736,7 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
 
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
-  dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(256);
+  dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(512);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)
 #undef L

@@ -125,18 +125,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 // full tile are computed once; the tile's first row only moves a uniform
 // base.  A tile that runs past `row_limit` takes a slow path that clamps rows
 // to row_limit - 1 (callers mask those rows), so every address is valid;
-// row_limit must be >= 1.  `w` must be wave-uniform.
-template <int D, int ROWS, typename T> struct TileLoader {
+// row_limit must be >= 1.  NW waves (w = 0 .. NW-1) share the loads; `w`
+// must be wave-uniform.
+template <int D, int ROWS, typename T, int NW = 4> struct TileLoader {
   static constexpr int CPR = Lds<D>::CPR;
-  static constexpr int PER_WAVE = ROWS * CPR / 256;
-  static_assert(ROWS * CPR % 256 == 0, "tile must split into whole wave loads");
+  static constexpr int PER_WAVE = ROWS * CPR / (64 * NW);
+  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
   static constexpr int LOWMASK = (D % 128 == 0) ? 15 : 7;
   const char* g;
   int64_t stride_b;  // row stride in bytes
   uint32_t voff[PER_WAVE];
 
   __device__ __forceinline__ static void coords(int j, int w, int lane, int& row, int& c) {
-    const int L = 64 * (4 * j + w) + lane;
+    const int L = 64 * (NW * j + w) + lane;
     row = L / CPR;
     const int phys = L % CPR;
     c = (phys & ~LOWMASK) | ((phys ^ Lds<D>::swz(row)) & LOWMASK);
@@ -157,7 +158,7 @@ template <int D, int ROWS, typename T> struct TileLoader {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j)
         __builtin_amdgcn_global_load_lds((const void*)(base + voff[j]),
-                                         (lds_void*)(tile + 512 * (4 * j + w)), 16, 0, 0);
+                                         (lds_void*)(tile + 512 * (NW * j + w)), 16, 0, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
@@ -166,7 +167,7 @@ template <int D, int ROWS, typename T> struct TileLoader {
         int gr = row0 + row;
         gr = gr < row_limit ? gr : row_limit - 1;
         __builtin_amdgcn_global_load_lds((const void*)(g + gr * stride_b + 16 * c),
-                                         (lds_void*)(tile + 512 * (4 * j + w)), 16, 0, 0);
+                                         (lds_void*)(tile + 512 * (NW * j + w)), 16, 0, 0);
       }
     }
   }
@@ -225,6 +226,18 @@ __device__ __forceinline__ u32x4 lds_trA(const T* buf, int kb, int mb, int lane)
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
+// 32-bit LDS byte address of a pointer into __shared__ memory, and loads
+// from such an address.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+__device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
+__device__ __forceinline__ s16x4 lds_tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+}
+
 // Register-lean readers for the two A-operand patterns above.  For rows of
 // 64 or 128 elements the swizzled byte offset of every access a lane makes
 // is (per-lane base) XOR (compile-time constant) plus a compile-time row
@@ -242,6 +255,22 @@ template <int D, typename T> struct RowReader {
     lane_ = lane;
     const int row = sig(lane & 31), g = lane >> 5;
     pre = (uint32_t)(row * D * 2 + 16 * (g ^ Lds<D>::swz(row)));
+  }
+  // A tile whose buffer changes from trip to trip: the buffer's address is
+  // folded into the per-lane offset once (one VALU op) and each read then
+  // costs at most one XOR.  Buffers must be 256-byte aligned, so that adding
+  // the base leaves the XORed bits alone.
+  struct View {
+    uint32_t bp;
+    const T* tile;
+    int lane;
+    template <int T_> __device__ __forceinline__ u32x4 read(int mb) const {
+      if constexpr (FAST) return lds_load16(xor_at_use<32u * T_>(bp) + (uint32_t)(mb * D * 2));
+      else return lds_rowA<D>(tile, mb, 16 * T_, lane);
+    }
+  };
+  __device__ __forceinline__ View view(const T* tile) const {
+    return View{lds_addr(tile) + pre, tile, lane_};
   }
   // X[mb + sig(l32)][16 t + 8g + e]; mb a multiple of 32
   template <int T_>
@@ -268,6 +297,27 @@ template <int D, typename T> struct TrReader {
       const int col = 16 * (G & 1) + 4 * (i & 3);
       pre[h] = (uint32_t)(2 * Lds<D>::off(row, col));
     }
+  }
+  struct View {
+    uint32_t bp0, bp1;
+    const T* tile;
+    int lane;
+    template <int MB> __device__ __forceinline__ u32x4 read(int kb) const {
+      if constexpr (FAST) {
+        constexpr uint32_t x = (uint32_t)(64 * (MB / 32));
+        const uint32_t kbo = (uint32_t)(kb * D * 2);
+        s16x4 lo = lds_tr8(xor_at_use<x>(bp0) + kbo), hi = lds_tr8(xor_at_use<x>(bp1) + kbo);
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+      } else {
+        return lds_trA<D>(tile, kb, MB, lane);
+      }
+    }
+  };
+  // as RowReader::view (256-byte aligned buffers)
+  __device__ __forceinline__ View view(const T* tile) const {
+    const uint32_t base = lds_addr(tile);
+    return View{base + pre[0], base + pre[1], tile, lane_};
   }
   // X[kb + 8g + e][MB + l32], e = 0..7; kb a multiple of 16, MB of 32
   template <int MB>
