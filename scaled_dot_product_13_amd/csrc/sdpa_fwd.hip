@@ -86,7 +86,12 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   const uint32_t bh = (uint32_t)(b * a.H + h);
   if (DROP) dk = drop_key(a.drop);
   const float c = a.scale_log2;
-  const bool pos = c >= 0.f;  // uniform: which extreme of the raw scores is the max
+  // A zero scale makes every visible score equal; the exponent's FMA cannot
+  // then hide a score with an infinity (0 * inf), so such tiles replace the
+  // raw scores by 0 (visible) / -inf (hidden) and use an effective scale 1.
+  const bool zs = c == 0.f;
+  const float ce = zs ? 1.f : c;
+  const bool pos = ce >= 0.f;  // uniform: which extreme of the raw scores is the max
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -167,8 +172,6 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     // Scores in scaled log2 units.  Without bias the scale is folded into
     // the exponent's FMA and the row max is taken on the raw scores.
     const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > wq0);
-    // element (blk, r) holds key n0 + 8g + koff(blk, r); it is visible iff
-    // koff <= lim (key < s_kv and, causal, key <= row)
     auto visible = [&](int blk, int r) {
       int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
       return kv < skv && (!CAUSAL || kv <= row);
@@ -198,12 +201,12 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       mrow = max_pair32(mx);
     } else {
       const float hide = pos ? -INFINITY : INFINITY;
-      if (need_mask) {
+      if (need_mask || zs) {
         keep_branch();
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : hide;
+          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? (zs ? 0.f : s[blk][r]) : hide;
       }
       float mx = -INFINITY, mn = INFINITY;
       if (pos) {
@@ -212,14 +215,14 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
         mx = max_pair32(mx);
-        mrow = mx == -INFINITY ? -INFINITY : mx * c;
+        mrow = mx == -INFINITY ? -INFINITY : mx * ce;
       } else {
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mn = fminf(mn, s[blk][r]);
         mn = -max_pair32(-mn);
-        mrow = mn == INFINITY ? -INFINITY : mn * c;
+        mrow = mn == INFINITY ? -INFINITY : mn * ce;
       }
     }
 
@@ -241,44 +244,34 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       m_run = m_new;
     }
     // Masked scores already hold -inf (scaled) / the hiding infinity (raw),
-    // so the exponent loop has no branches.  A zero scale is the one case
-    // where c * (+-inf) is not -inf; it is fixed up after the loop.
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[blk][r] = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
-                         : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_run));
-    if (!BIAS && need_mask && c == 0.f) {
-      keep_branch();
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : 0.f;
-    }
+    // so the exponent loop has no branches.  One 16-key slice at a time: the
+    // slice's P V products are issued as soon as it is packed, so they run
+    // on the matrix cores while the next slice's exponentials are computed.
     float psum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) psum += s[blk][r];
-    l_run += psum;
-    if (DROP) {
-#pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
-          bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
-          s[blk][r] = keep ? s[blk][r] : 0.f;
-        }
-    }
     u32x4 pb[2 * NBLK];
+    static_for<2 * NBLK>([&](auto tt) __attribute__((always_inline)) {
+      constexpr int blk = tt / 2, r0 = 8 * (tt % 2);
+      float p[8];
 #pragma unroll
-    for (int tt = 0; tt < 2 * NBLK; ++tt) {
-      int blk = tt >> 1, r0 = 8 * (tt & 1);
+      for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        const float x = BIAS ? __builtin_amdgcn_exp2f(s[blk][r] - m_run)
+                             : __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], ce, -m_run));
+        psum += x;
+        p[e] = x;
+        if (DROP) {
+          const int k = 4 * blk + 2 * (r >> 3) + ((r & 7) >> 2);
+          const bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
+          p[e] = keep ? x : 0.f;
+        }
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(s[blk][r0 + 2 * e], s[blk][r0 + 2 * e + 1]);
-    }
+      for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(p[2 * e], p[2 * e + 1]);
+      // O^T += V^T P^T for this slice
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb[tt], oacc[db]);
+    });
+    l_run += psum;
 
     if (DROP && a.keep && row_ok) {
       uint8_t* kp = a.keep + (((int64_t)b * a.H + h) * a.seq.s_q + row) * a.seq.s_kv;
@@ -294,12 +287,6 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       }
     }
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int tt = 0; tt < 2 * NBLK; ++tt) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb[tt], oacc[db]);
-    }
   };
 
   for (int it = 0; it < nt; it += 2) {
