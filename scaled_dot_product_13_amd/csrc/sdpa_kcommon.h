@@ -49,29 +49,36 @@ __device__ __forceinline__ int64_t row_stat_base(const SeqInfo& s, const SeqPos&
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-// L2.  The tile kernels use a 1-D grid and give XCD x a contiguous range of
-// the (batch*head, tile) work list, so all tiles of one head - which read the
-// same K/V (or Q/dO) tiles - run behind one L2.  Any bijection is correct;
-// this one only changes which L2 serves which head.
+// L2, and each XCD starts its workgroups in increasing id order.  The tile
+// kernels use a 1-D grid in which XCD x = id mod 8 owns a contiguous range
+// of (batch, head) pairs, so every tile of a head - which all read the same
+// K/V (or Q/dO) - runs behind one L2.  Within an XCD the tiles are ordered
+// rank-major: rank r of every owned head before rank r + 1.  The kernels
+// number ranks heaviest first under a causal mask, so this is largest-first
+// list scheduling over the XCD's compute units; head-major order would start
+// the last heads' heaviest tiles last and leave the machine idle at the end.
+// Any bijection is correct; this one only changes placement and order.
 struct WorkItem {
   int b, h, tile;
   bool valid;
 };
 __device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B) {
-  const int total = ntiles * H * B;
-  const int lin = blockIdx.x, per = (total + 7) / 8;
-  const int logical = (lin & 7) * per + (lin >> 3);
+  const int BH = B * H;
+  const int x = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  const int h_lo = (int)((int64_t)x * BH / 8);
+  const int nh = (int)((int64_t)(x + 1) * BH / 8) - h_lo;  // heads owned by XCD x
   WorkItem wi;
-  wi.valid = logical < total;
-  const int hb = logical / ntiles;
-  wi.tile = logical - hb * ntiles;
+  wi.valid = nh > 0 && pos < nh * ntiles;
+  const int r = nh > 0 ? pos / nh : 0;
+  const int hb = h_lo + (pos - r * nh);
+  wi.tile = r;
   wi.b = hb / H;
   wi.h = hb - wi.b * H;
   return wi;
 }
 inline dim3 xcd_grid(int ntiles, int H, int B) {
-  const long total = (long)ntiles * H * B;
-  return dim3((unsigned)((total + 7) / 8 * 8), 1, 1);
+  const long BH = (long)B * H;
+  return dim3((unsigned)(8 * ((BH + 7) / 8) * ntiles), 1, 1);
 }
 
 struct DropKey {
