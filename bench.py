@@ -2,7 +2,8 @@
 
 One step = one pass of the whole hot path over one batch of the headline
 workload (bf16, causal, B=4 H=16 S_q=S_kv=2048 d=128, scale 1/sqrt(128)):
-sdpa_fwd, then the backward's three kernels (D preprocess, dK/dV, dQ).
+sdpa_fwd, then the backward's two kernels in the order sdpa_bwd runs them
+(dQ with the D preprocess of its rows, then dK/dV).
 Inputs are seeded synthetic N(0,1) tensors, resident in HBM before timing.
 
 Throughput uses the workload's algorithmic flop count: forward
@@ -117,23 +118,22 @@ def main():
     stats = torch.empty(off + n, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd_dq", "bwd_dkdv")
     ev = {n: [] for n in names}
 
     def step(record):
         """fwd, then the backward's kernels; with `record`, HIP events on the
         launch stream bracket every kernel."""
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         calls = (lambda: S.sdpa_fwd(q, k, v, out=o, lse=lse, **kw),
-                 lambda: S.sdpa_bwd_preprocess(o, do, lse, out=stats),
-                 lambda: S.sdpa_bwd_dkdv(q, k, v, do, stats, dk=dk, dv=dv, **kw),
-                 lambda: S.sdpa_bwd_dq(q, k, v, do, stats, dq=dq, **kw))
+                 lambda: S.sdpa_bwd_dq_preprocess(q, k, v, o, do, lse, dq=dq, stats=stats, **kw),
+                 lambda: S.sdpa_bwd_dkdv(q, k, v, do, stats, dk=dk, dv=dv, **kw))
         for i, c in enumerate(calls):
             if record:
                 e[i].record(stream)
             c()
         if record:
-            e[4].record(stream)
+            e[3].record(stream)
             for i, n in enumerate(names):
                 ev[n].append((e[i], e[i + 1]))
 
@@ -157,7 +157,7 @@ def main():
 
     f_fl, b_fl = flops(wl)
     fwd_ms = avg["fwd"]
-    bwd_ms = avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+    bwd_ms = avg["bwd_dq"] + avg["bwd_dkdv"]
     value = (f_fl + b_fl) / (ms_step * 1e-3) / 1e12
     fwd_tf = f_fl / (fwd_ms * 1e-3) / 1e12
     bwd_tf = b_fl / (bwd_ms * 1e-3) / 1e12
@@ -167,13 +167,10 @@ def main():
     per_kernel_flops = {
         "fwd": 2.0 * s2 * (wl.d_qk + wl.d_v),                 # Q K^T and P V
         "bwd_dkdv": 2.0 * s2 * (2 * wl.d_qk + 2 * wl.d_v),    # S, dP, dV, dK
-        "bwd_dq": 2.0 * s2 * (2 * wl.d_qk + wl.d_v),          # S, dP, dQ
+        "bwd_dq": 2.0 * s2 * (2 * wl.d_qk + wl.d_v),          # S, dP, dQ (+ the D preprocess)
     }
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg[n])
     ach = per_kernel_flops[dom] / (avg[dom] * 1e-3) / 1e12
-    es = 2  # bytes per io element
-    # preprocess: reads O, dO (io) and LSE, writes D and LSE*log2e (fp32)
-    pre_bytes = 2 * wl.b * wl.h * wl.s_q * wl.d_v * es + 3 * 4 * wl.b * wl.h * wl.s_q
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_traffic(dom), "avg_launch_ms": round(avg[dom], 5)}
@@ -191,8 +188,7 @@ def main():
                 "pct_mfma_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(bwd_ms, 5), "tflops": round(bwd_tf, 2),
                 "pct_mfma_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2),
-                "kernels_ms": {n: round(avg[n], 5) for n in ("bwd_pre", "bwd_dkdv", "bwd_dq")},
-                "preprocess_GBps": round(pre_bytes / (avg["bwd_pre"] * 1e-3) / 1e9, 1)},
+                "kernels_ms": {n: round(avg[n], 5) for n in ("bwd_dq", "bwd_dkdv")}},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -165,20 +165,20 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t *problem,
  *   stats[0 .. n)        D = rowsum(dO o O), fp32 accumulation
  *   stats[m .. m + n)    softmax_lse * log2(e)   (m = n rounded up to 64)
  * in the layout of softmax_lse but with group mode rows [h, b*s_q] for both.
- * `stats` needs sdpa_bwd_workspace_size(problem) bytes; sdpa_bwd runs this
- * step itself into its workspace.  Errors as for sdpa_bwd. */
+ * `stats` needs sdpa_bwd_workspace_size(problem) bytes; sdpa_bwd does this
+ * step itself into its workspace (for 16-bit io inside its dQ kernel, see
+ * sdpa_bwd_dq_preprocess).  Errors as for sdpa_bwd. */
 sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t *problem,
                                   const void *o, sdpa_strides_t o_strides,
                                   const void *d_o, sdpa_strides_t do_strides,
                                   const float *softmax_lse, float *stats, void *stream);
 
-/* The backward's two main kernels, one call each.  sdpa_bwd runs
- * preprocess -> dK/dV -> dQ on one stream; the dK/dV and dQ kernels read only
- * the inputs and the stats, never each other's results, so a caller may
- * instead run sdpa_bwd_preprocess and then these two on two streams, or time
- * them one by one.  `stats` is the preprocess output above.
- * sdpa_bwd_dkdv writes dk, dv and (nullable) dbias; sdpa_bwd_dq writes dq.
- * Errors as for sdpa_bwd (no workspace argument). */
+/* The backward's two main kernels, one call each.  The dK/dV and dQ kernels
+ * read only the inputs and the stats, never each other's results, so a
+ * caller may run sdpa_bwd_preprocess and then these two in either order or
+ * on two streams, or time them one by one.  `stats` is the preprocess
+ * output above.  sdpa_bwd_dkdv writes dk, dv and (nullable) dbias;
+ * sdpa_bwd_dq writes dq.  Errors as for sdpa_bwd (no workspace argument). */
 sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t *problem,
                             const void *q, sdpa_strides_t q_strides,
                             const void *k, sdpa_strides_t k_strides,
@@ -199,6 +199,25 @@ sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t *problem,
                           const float *stats,
                           void *dq, sdpa_strides_t dq_strides,
                           void *stream);
+
+/* dQ and the preprocess in one kernel (16-bit io only; SDPA_ERR_UNSUPPORTED
+ * for fp32): each workgroup computes D = rowsum(dO o O) and LSE*log2(e) for
+ * the query rows it owns, writes them to `stats` (layout as for
+ * sdpa_bwd_preprocess, which it replaces) and then computes dq for those
+ * rows.  sdpa_bwd runs this and then sdpa_bwd_dkdv on the stats, saving a
+ * kernel and its launch gap.  D is summed in a different order from
+ * sdpa_bwd_preprocess, so the two agree to fp32 rounding, not bitwise.
+ * Errors as for sdpa_bwd_dq. */
+sdpa_status_t sdpa_bwd_dq_preprocess(const sdpa_problem_t *problem,
+                                     const void *q, sdpa_strides_t q_strides,
+                                     const void *k, sdpa_strides_t k_strides,
+                                     const void *v, sdpa_strides_t v_strides,
+                                     const void *attn_bias, sdpa_strides_t bias_strides,
+                                     const void *o, sdpa_strides_t o_strides,
+                                     const void *d_o, sdpa_strides_t do_strides,
+                                     const float *softmax_lse, float *stats,
+                                     void *dq, sdpa_strides_t dq_strides,
+                                     void *stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *sdpa_status_string(sdpa_status_t status);

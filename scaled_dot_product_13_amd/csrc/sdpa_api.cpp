@@ -315,9 +315,16 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
                  (long long)p->h, (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk,
                  (long long)p->d_v, p->is_causal, attn_bias != nullptr, dbias != nullptr,
                  (double)p->dropout_probability, group);
-  hipError_t e = sdpa::launch_bwd_pre(t, (int)p->d_v, a, s);
-  if (e == hipSuccess) e = sdpa::launch_bwd_dkdv(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
-  if (e == hipSuccess) e = sdpa::launch_bwd_dq(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+  hipError_t e;
+  if (t != sdpa::IoType::F32) {
+    // 16-bit io: the dQ kernel does the preprocess for its rows, then dK/dV
+    e = sdpa::launch_bwd_dq(t, (int)p->d_qk, (int)p->d_v, causal, a, s, true);
+    if (e == hipSuccess) e = sdpa::launch_bwd_dkdv(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+  } else {
+    e = sdpa::launch_bwd_pre(t, (int)p->d_v, a, s);
+    if (e == hipSuccess) e = sdpa::launch_bwd_dkdv(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+    if (e == hipSuccess) e = sdpa::launch_bwd_dq(t, (int)p->d_qk, (int)p->d_v, causal, a, s);
+  }
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }
@@ -399,6 +406,40 @@ sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t* p, const void* q, sdpa_strides_t
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
   hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
+  return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd_dq_preprocess(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
+                                     const void* k, sdpa_strides_t k_s, const void* v,
+                                     sdpa_strides_t v_s, const void* attn_bias,
+                                     sdpa_strides_t bias_s, const void* o, sdpa_strides_t o_s,
+                                     const void* d_o, sdpa_strides_t do_s,
+                                     const float* softmax_lse, float* stats, void* dq,
+                                     sdpa_strides_t dq_s, void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  if (p->dtype == SDPA_F32)
+    return fail(SDPA_ERR_UNSUPPORTED, "the fused dQ + preprocess kernel is for 16-bit io; use "
+                "sdpa_bwd_preprocess then sdpa_bwd_dq");
+  if ((st = check_bwd_inputs(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, d_o, do_s, stats)) != SDPA_OK)
+    return st;
+  if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, dq, dq_s, "dq", true)) != SDPA_OK) return st;
+  if (!softmax_lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null");
+  sdpa::BwdArgs a{};
+  fill_bwd_args(p, a);
+  a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o; a.dout = d_o;
+  a.lse = softmax_lse;
+  a.dvec = stats; a.lse2 = stats_lse2(p, stats);
+  a.dq = dq;
+  a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
+  a.so_ = to_str(o_s); a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s);
+  a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
+  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+                                     (hipStream_t)stream, true);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }

@@ -386,7 +386,11 @@ template <int DQK, int DV, bool DROP> struct DqOcc {
   static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
 };
 
-template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+//
+// With PRE the kernel also does the preprocess for its rows: D from the O
+// and dO rows it loads and LSE*log2(e) from the forward's LSE, both written
+// to the stats for the dK/dV kernel, which then runs after it.
+template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP, bool PRE>
 __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(const BwdArgs a) {
   constexpr int BR = 128, BC = 64;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32;
@@ -425,8 +429,32 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   for (int t = 0; t < VT; ++t)
     doreg[t] = row_ok ? *(const u32x4*)(dog + (int64_t)row * a.sdo_.s + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
   float lse2 = 0.f, Drow = 0.f;
-  if (row_ok) {
-    const int64_t st = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + row;
+  const int64_t st = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q) + row;
+  if (PRE) {
+    // D_row = rowsum(dO o O): this lane holds chunks 2t + g of its row's dO
+    // (the B-operand layout), so it dots the same chunks of O and adds the
+    // other half from lane l ^ 32.
+    float part = 0.f;
+    if (row_ok) {
+      const T* orow = base_ptr<T>(a.o, a.so_, sp, h, true) + (int64_t)row * a.so_.s;
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        const u32x4 ov = *(const u32x4*)(orow + 16 * t + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          part += to_f32<T>((uint16_t)(ov[e] & 0xffffu)) * to_f32<T>((uint16_t)(doreg[t][e] & 0xffffu));
+          part += to_f32<T>((uint16_t)(ov[e] >> 16)) * to_f32<T>((uint16_t)(doreg[t][e] >> 16));
+        }
+      }
+      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      lse2 = a.lse[lb + row] * kLog2e;
+    }
+    Drow = sum_pair32(part);
+    if (row_ok && g == 0) {
+      a.dvec[st] = Drow;
+      a.lse2[st] = lse2;
+    }
+  } else if (row_ok) {
     lse2 = a.lse2[st];
     Drow = a.dvec[st];
   }
@@ -743,9 +771,15 @@ static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a,
   return hipErrorInvalidValue;
 }
 template <typename T, int DQK, int DV>
-static hipError_t dq_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
+static hipError_t dq_dims(bool causal, bool bias, bool drop, bool pre, const BwdArgs& a,
+                          hipStream_t st) {
   dim3 grid = xcd_grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
-#define L(C, BI, DR) { hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
+#define L(C, BI, DR)                                                                        \
+  {                                                                                         \
+    if (pre) hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR, true>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR, false>), grid, block, 0, st, a);    \
+    return hipGetLastError();                                                               \
+  }
   SDPA_FLAG_SWITCH(L)
 #undef L
   return hipErrorInvalidValue;
@@ -760,11 +794,11 @@ static hipError_t dkdv_type(int dqk, int dv, bool causal, bool bias, bool drop, 
   return hipErrorInvalidValue;
 }
 template <typename T>
-static hipError_t dq_type(int dqk, int dv, bool causal, bool bias, bool drop, const BwdArgs& a,
-                          hipStream_t st) {
-  if (dqk == 64 && dv == 64) return dq_dims<T, 64, 64>(causal, bias, drop, a, st);
-  if (dqk == 128 && dv == 128) return dq_dims<T, 128, 128>(causal, bias, drop, a, st);
-  if (dqk == 192 && dv == 128) return dq_dims<T, 192, 128>(causal, bias, drop, a, st);
+static hipError_t dq_type(int dqk, int dv, bool causal, bool bias, bool drop, bool pre,
+                          const BwdArgs& a, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return dq_dims<T, 64, 64>(causal, bias, drop, pre, a, st);
+  if (dqk == 128 && dv == 128) return dq_dims<T, 128, 128>(causal, bias, drop, pre, a, st);
+  if (dqk == 192 && dv == 128) return dq_dims<T, 192, 128>(causal, bias, drop, pre, a, st);
   return hipErrorInvalidValue;
 }
 
@@ -779,10 +813,12 @@ hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st,
+                         bool with_pre) {
   const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
-  if (t == IoType::BF16) return dq_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
-  if (t == IoType::F16) return dq_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
+  if (t == IoType::BF16) return dq_type<__bf16>(dqk, dv, causal, bias, drop, with_pre, a, st);
+  if (t == IoType::F16) return dq_type<_Float16>(dqk, dv, causal, bias, drop, with_pre, a, st);
+  if (with_pre) return hipErrorInvalidValue;  // the fp32 path keeps the separate preprocess
   dim3 grid((a.seq.s_q + 3) / 4, a.H, a.B), block(256);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dq_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)

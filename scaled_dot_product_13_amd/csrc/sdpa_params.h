@@ -68,8 +68,10 @@ hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a,
 hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs& a,
                            hipStream_t st);
+// with_pre: the dQ kernel also writes the stats (D, LSE*log2e) of its rows
+// from o, dout and lse (16-bit io only)
 hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a,
-                         hipStream_t st);
+                         hipStream_t st, bool with_pre = false);
 bool mfma_dims_supported(int dqk, int dv);
 
 }  // namespace sdpa

@@ -69,6 +69,9 @@ _lib.sdpa_bwd_dkdv.restype = ctypes.c_int
 _lib.sdpa_bwd_dq.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
                              _vp, Strides, _vp, _vp, Strides, _vp]
 _lib.sdpa_bwd_dq.restype = ctypes.c_int
+_lib.sdpa_bwd_dq_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                                        _vp, Strides, _vp, Strides, _vp, _vp, _vp, Strides, _vp]
+_lib.sdpa_bwd_dq_preprocess.restype = ctypes.c_int
 _lib.sdpa_status_string.argtypes = [ctypes.c_int]
 _lib.sdpa_status_string.restype = ctypes.c_char_p
 _lib.sdpa_last_error_message.restype = ctypes.c_char_p
@@ -253,6 +256,24 @@ def sdpa_bwd_dkdv(q, k, v, dout, stats, *, bias=None, dk=None, dv=None, dbias=No
                               _ptr(dk), _strides(dk, group), _ptr(dv), _strides(dv, group),
                               _ptr(dbias), _strides(dbias, False), _stream()))
     return dk, dv, dbias
+
+
+def sdpa_bwd_dq_preprocess(q, k, v, o, dout, lse, *, bias=None, dq=None, stats=None, **kw):
+    """dQ and, for the same rows, the backward stats in one kernel (16-bit io).
+    Returns (dq, stats); run sdpa_bwd_dkdv on the stats afterwards."""
+    group = kw.get("cu_seqlens_q") is not None
+    p = make_problem(q, k, v, **kw)
+    dq = _alloc_like(q, q.shape) if dq is None else dq
+    n, off = stats_layout(p.b, p.h, p.s_q)
+    if stats is None:
+        stats = torch.empty(off + n, dtype=torch.float32, device=q.device)
+    assert stats.numel() >= off + n and stats.dtype == torch.float32 and stats.is_contiguous()
+    _check(_lib.sdpa_bwd_dq_preprocess(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k),
+                                       _strides(k, group), _ptr(v), _strides(v, group), _ptr(bias),
+                                       _strides(bias, False), _ptr(o), _strides(o, group),
+                                       _ptr(dout), _strides(dout, group), _ptr(lse), _ptr(stats),
+                                       _ptr(dq), _strides(dq, group), _stream()))
+    return dq, stats
 
 
 def sdpa_bwd_dq(q, k, v, dout, stats, *, bias=None, dq=None, **kw):

@@ -245,18 +245,53 @@ def test_preprocess_matches_oracle_D(S):
 
 
 def test_split_backward_equals_sdpa_bwd(S):
-    # preprocess + dK/dV + dQ entry points give bitwise the results of sdpa_bwd
+    # the fused dQ + preprocess entry point followed by dK/dV gives bitwise
+    # the results of sdpa_bwd (which runs the same two kernels); the separate
+    # preprocess path agrees to the fp32 rounding of D
     wl = inputs.small("f16", b=2, h=2, s_q=200, s_kv=260, bias=True, dropout_p=0.1, seed=31)
     x = inputs.make_inputs(wl)
     q, k, v, do, bias = (x[n].cuda() for n in ("q", "k", "v", "dout", "bias"))
     kw = dict(causal=False, dropout_p=0.1, seed=5, offset=2)
     o, lse, _ = S.sdpa_fwd(q, k, v, bias=bias, **kw)
     dq, dk, dv, db = S.sdpa_bwd(q, k, v, o, do, lse, bias=bias, want_dbias=True, **kw)
-    stats = S.sdpa_bwd_preprocess(o, do, lse)
+    dq2, stats = S.sdpa_bwd_dq_preprocess(q, k, v, o, do, lse, bias=bias, **kw)
     dk2, dv2, db2 = S.sdpa_bwd_dkdv(q, k, v, do, stats, bias=bias, want_dbias=True, **kw)
-    dq2 = S.sdpa_bwd_dq(q, k, v, do, stats, bias=bias, **kw)
+    stats3 = S.sdpa_bwd_preprocess(o, do, lse)
+    dk3, dv3, db3 = S.sdpa_bwd_dkdv(q, k, v, do, stats3, bias=bias, want_dbias=True, **kw)
+    dq3 = S.sdpa_bwd_dq(q, k, v, do, stats3, bias=bias, **kw)
     torch.cuda.synchronize()
     for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2), (db, db2)):
+        assert torch.equal(a_, b_)
+    n, off = S.stats_layout(2, 2, 200)
+    assert torch.equal(stats[off:off + n], stats3[off:off + n])  # LSE*log2(e): same product
+    assert torch.max(torch.abs(stats[:n] - stats3[:n])).item() <= 1e-5 * max(1.0, stats3[:n].abs().max().item())
+    for a_, b_ in ((dq, dq3), (dk, dk3), (dv, dv3), (db, db3)):
+        assert torch.max(torch.abs(a_.float() - b_.float())).item() <= 2e-3
+
+
+def test_fused_preprocess_stats_group_mode(S):
+    # the dQ kernel's own stats in group (varlen) mode equal the separate
+    # preprocess's up to the fp32 rounding of D
+    lengths = [37, 130, 1, 64]
+    wl = inputs.small("bf16", b=len(lengths), h=3, d_qk=64, d_v=64, causal=True, seed=41,
+                      varlen=(len(lengths), 1, 130))
+    x = inputs.make_inputs(wl, lengths=lengths)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "dout"))
+    cu = x["cu_seqlens"].cuda()
+    L = x["max_seqlen"]
+    gkw = dict(causal=True, cu_seqlens_q=cu, cu_seqlens_kv=cu, max_seqlen_q=L, max_seqlen_kv=L)
+    o, lse, _ = S.sdpa_fwd(q, k, v, **gkw)
+    _, stats = S.sdpa_bwd_dq_preprocess(q, k, v, o, do, lse, **gkw)
+    stats3 = S.sdpa_bwd_preprocess(o, do, lse, cu_seqlens_q=cu, max_seqlen_q=L)
+    torch.cuda.synchronize()
+    n, off = S.stats_layout(len(lengths), 3, L)
+    T = sum(lengths)
+    for h in range(3):  # rows [h, 0 .. T) of each half are written
+        a_ = stats[h * len(lengths) * L: h * len(lengths) * L + T]
+        b_ = stats3[h * len(lengths) * L: h * len(lengths) * L + T]
+        assert torch.max(torch.abs(a_ - b_)).item() <= 1e-5 * max(1.0, b_.abs().max().item())
+        a_ = stats[off + h * len(lengths) * L: off + h * len(lengths) * L + T]
+        b_ = stats3[off + h * len(lengths) * L: off + h * len(lengths) * L + T]
         assert torch.equal(a_, b_)
 
 
