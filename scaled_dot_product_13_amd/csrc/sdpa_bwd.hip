@@ -192,10 +192,31 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     const int q0 = q_begin + i * BQ, set = i % NSET;
     const auto vQ = rdQ.view(sQ[set]);
     const auto vOt = rdOt.view(sO[set]);
+    // Operand reads issue in source order (their address XORs are volatile),
+    // so each phase's operands are all requested before its products, and
+    // the dV operands before the element-wise work.
+    // (in two halves when there are more than 8 operands, to bound registers)
+    constexpr int KH = KT > 8 ? KT / 2 : KT;
+    u32x4 qop[KH];
     f32x16 s = f32x16{};
-    static_for<KT>([&](auto t) __attribute__((always_inline)) {
-      s = mfma32<T>(vQ.template read<t>(0), reg[t], s);
+    static_for<KT / KH>([&](auto hf) __attribute__((always_inline)) {
+      static_for<KH>([&](auto j) __attribute__((always_inline)) {
+        qop[j] = vQ.template read<hf * KH + j>(0);
+      });
+#pragma unroll
+      for (int j = 0; j < KH; ++j) s = mfma32<T>(qop[j], reg[hf * KH + j], s);
     });
+    // dV operands: requested before the element-wise work, unless the
+    // element-wise work itself needs the registers (bias, wide Q/K rows)
+    constexpr bool EARLY_O = !BIAS && DQK <= 128;
+    u32x4 oop[2 * VB];
+    auto read_oop = [&]() __attribute__((always_inline)) {
+      static_for<VB>([&](auto vb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) oop[tt * VB + vb] = vOt.template read<32 * vb>(16 * tt);
+      });
+    };
+    if constexpr (EARLY_O) read_oop();
     uint32_t kw[8];
     if (DROP) {
       // 4x4 patches along this lane's queries (the first 4 of the 8 used)
@@ -265,10 +286,11 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         }
     }
     // dV^T += dO^T (P o Z)
-    static_for<VB>([&](auto vb) __attribute__((always_inline)) {
+    if constexpr (!EARLY_O) read_oop();
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) acc[vb] = mfma32<T>(vOt.template read<32 * vb>(16 * tt), pb[tt], acc[vb]);
-    });
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma32<T>(oop[tt * VB + vb], pb[tt], acc[vb]);
   };
 
   // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
@@ -276,9 +298,23 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     const int q0 = q_begin + i * BQ, set = i % NSET;
     const auto vO = rdO.view(sO[set]);
     const auto vQt = rdQt.view(sQ[set]);
+    // (in halves when the dK accumulator is large, to bound registers)
+    constexpr int VH = QB > 4 ? VT / 2 : VT;
+    u32x4 oop[VH];
     f32x16 dp = f32x16{};
-    static_for<VT>([&](auto t) __attribute__((always_inline)) {
-      dp = mfma32<T>(vO.template read<t>(0), reg[t], dp);
+    static_for<VT / VH>([&](auto hf) __attribute__((always_inline)) {
+      static_for<VH>([&](auto j) __attribute__((always_inline)) {
+        oop[j] = vO.template read<hf * VH + j>(0);
+      });
+#pragma unroll
+      for (int j = 0; j < VH; ++j) dp = mfma32<T>(oop[j], reg[hf * VH + j], dp);
+    });
+    // Q^T operands for dK (the first half of them when there are more than 8)
+    constexpr int QH = QB > 4 ? QB / 2 : QB;
+    u32x4 qtop[2 * QH];
+    static_for<QH>([&](auto qb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + qb] = vQt.template read<32 * qb>(16 * tt);
     });
     const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
     u32x4 pw[4];
@@ -314,10 +350,20 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       for (int e = 0; e < 4; ++e) dsb[hh][e] = pack2<T>(ds[2 * e], ds[2 * e + 1]);
     }
     // dK^T += Q^T dS
-    static_for<QB>([&](auto qb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) acc[qb] = mfma32<T>(vQt.template read<32 * qb>(16 * tt), dsb[tt], acc[qb]);
-    });
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int qb = 0; qb < QH; ++qb) acc[qb] = mfma32<T>(qtop[tt * QH + qb], dsb[tt], acc[qb]);
+    if constexpr (QH < QB) {
+      static_for<QB - QH>([&](auto j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + j] = vQt.template read<32 * (QH + j)>(16 * tt);
+      });
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < QB - QH; ++j) acc[QH + j] = mfma32<T>(qtop[tt * QH + j], dsb[tt], acc[QH + j]);
+    }
   };
 
   if (nq > 0) issue(0);
