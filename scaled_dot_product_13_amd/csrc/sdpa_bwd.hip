@@ -23,6 +23,14 @@
 // FmhaBwdConvertQGradKernel, and oneDNN adds fp32 dQ atomically.
 #include "sdpa_kcommon.h"
 
+// heads whose tiles are interleaved rank-major on one XCD (see xcd_work)
+#ifndef SDPA_DKDV_HEAD_GROUP
+#define SDPA_DKDV_HEAD_GROUP 2
+#endif
+#ifndef SDPA_DQ_HEAD_GROUP
+#define SDPA_DQ_HEAD_GROUP 4
+#endif
+
 namespace sdpa {
 
 // ---------------------------------------------------------------------------
@@ -103,7 +111,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   const int w = wave_id();
   const int kb = w & 3;
   const bool roleA = w < 4;
-  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H, a.B);
+  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H, a.B, SDPA_DKDV_HEAD_GROUP);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const SeqPos sp = resolve_seq(a.seq, b);
@@ -446,7 +454,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B);
+  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_DQ_HEAD_GROUP);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first

@@ -22,6 +22,10 @@
 #ifndef SDPA_FWD_NBLK
 #define SDPA_FWD_NBLK 2
 #endif
+// heads whose tiles are interleaved rank-major on one XCD (see xcd_work)
+#ifndef SDPA_FWD_HEAD_GROUP
+#define SDPA_FWD_HEAD_GROUP 4
+#endif
 
 namespace sdpa {
 
@@ -47,7 +51,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B);
+  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first

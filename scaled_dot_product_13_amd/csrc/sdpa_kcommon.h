@@ -52,25 +52,30 @@ __device__ __forceinline__ int64_t row_stat_base(const SeqInfo& s, const SeqPos&
 // L2, and each XCD starts its workgroups in increasing id order.  The tile
 // kernels use a 1-D grid in which XCD x = id mod 8 owns a contiguous range
 // of (batch, head) pairs, so every tile of a head - which all read the same
-// K/V (or Q/dO) - runs behind one L2.  Within an XCD the tiles are ordered
-// rank-major: rank r of every owned head before rank r + 1.  The kernels
-// number ranks heaviest first under a causal mask, so this is largest-first
-// list scheduling over the XCD's compute units; head-major order would start
-// the last heads' heaviest tiles last and leave the machine idle at the end.
-// Any bijection is correct; this one only changes placement and order.
+// K/V (or Q/dO) - runs behind one L2.  Within an XCD the heads go in groups
+// of G, and within a group the tiles are ordered rank-major: rank r of every
+// head of the group before rank r + 1.  The kernels number ranks heaviest
+// first under a causal mask, so this is largest-first list scheduling over
+// the XCD's compute units (head-major order starts the last heads' heaviest
+// tiles last and leaves the machine idle at the end), while G bounds how
+// many heads' tiles share the L2 at a time.  Any bijection is correct; this
+// one only changes placement and order.
 struct WorkItem {
   int b, h, tile;
   bool valid;
 };
-__device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B) {
+__device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B, int G) {
   const int BH = B * H;
   const int x = blockIdx.x & 7, pos = blockIdx.x >> 3;
   const int h_lo = (int)((int64_t)x * BH / 8);
   const int nh = (int)((int64_t)(x + 1) * BH / 8) - h_lo;  // heads owned by XCD x
   WorkItem wi;
   wi.valid = nh > 0 && pos < nh * ntiles;
-  const int r = nh > 0 ? pos / nh : 0;
-  const int hb = h_lo + (pos - r * nh);
+  const int gi = pos / (G * ntiles);           // head group
+  const int off = pos - gi * G * ntiles;
+  const int gsz = max(1, min(G, nh - gi * G));  // the last group may be smaller
+  const int r = off / gsz;
+  const int hb = h_lo + gi * G + (off - r * gsz);
   wi.tile = r;
   wi.b = hb / H;
   wi.h = hb - wi.b * H;
