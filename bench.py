@@ -62,11 +62,12 @@ def stored_traffic(kernel):
 
 def cpu_baseline(wl, x, budget_heads):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workload: every head of batch entry 0 up to `budget_heads` heads."""
+    workload: the first `budget_heads` (batch, head) slices in batch-major
+    order (by default all of them, i.e. the whole workload)."""
     import numpy as np
     import oracle.sdpa_oracle as O
     nthreads = min(16, os.cpu_count() or 1)
-    heads = [(0, h) for h in range(min(budget_heads, wl.h))]
+    heads = [(b, h) for b in range(wl.b) for h in range(wl.h)][:budget_heads]
     q, k, v, do = (x[n].double().numpy() for n in ("q", "k", "v", "dout"))
     kw = dict(scale=wl.softmax_scale, causal=wl.causal, heads=heads, threads=nthreads)
     t0 = time.perf_counter()
@@ -78,7 +79,7 @@ def cpu_baseline(wl, x, budget_heads):
     return {"value": round((f + b) * frac / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle",
             "sample": f"fwd+bwd of {len(heads)} of {wl.b * wl.h} (batch, head) slices of the "
-                      f"same workload (batch entry 0), fp64, {dt:.1f} s wall"}
+                      f"same workload, fp64, {dt:.1f} s wall"}
 
 
 def main():
@@ -88,7 +89,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload index (2 = headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-heads", type=int, default=1 << 30,
+                    help="(batch, head) slices the CPU baseline times (default: all)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
