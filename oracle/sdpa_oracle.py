@@ -174,10 +174,48 @@ def _run(fn, heads, threads):
     getattr(lib(), fn)(arr, len(heads), int(threads))
 
 
+def _kv_ratio(q, k, group):
+    """Query heads per key/value head (grouped-query attention).  Query head h
+    reads key/value head h // ratio: Composable Kernel's i_nhead /
+    nhead_ratio_qk in FmhaBwdDQDKDVKernel's pointer set-up; oneDNN's
+    kv_group_size = query heads / key-value heads in init_conf_common."""
+    ax = 1
+    hq, hk = q.shape[ax], k.shape[ax]
+    assert hq % hk == 0, "query heads must be a multiple of key/value heads"
+    return hq // hk
+
+
+def _repeat_kv(t, r):
+    """Key/value tensor with each head repeated r times along the head axis,
+    so that query head h sees head h // r (plain grouped-query definition)."""
+    return t if r == 1 else np.repeat(t, r, axis=1)
+
+
+def _sum_groups(t, r, complete):
+    """Per-query-head gradient [.., H, ..] summed over each group of r
+    consecutive heads (ascending order, fp64) into [.., H/r, ..].  Groups
+    with a head outside `complete` are NaN."""
+    if r == 1:
+        return t
+    shp = list(t.shape)
+    shp[1:2] = [shp[1] // r, r]
+    out = np.zeros(shp[:2] + shp[3:])
+    tt = t.reshape(shp)
+    for j in range(r):
+        out += tt[:, :, j]
+    for hk in range(out.shape[1]):
+        if not complete(hk):
+            out[:, hk] = np.nan
+    return out
+
+
 def fwd(q, k, v, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0,
         cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_keep=False):
-    """Forward definition.  Returns dict(o=..., lse=..., [keep=...])."""
+    """Forward definition.  Returns dict(o=..., lse=..., [keep=...]).
+    k and v may have fewer heads than q (grouped-query attention)."""
     q, k, v, bias = _as64(q), _as64(k), _as64(v), _as64(bias)
+    r = _kv_ratio(q, k, cu_seqlens_q is not None)
+    k, v = np.ascontiguousarray(_repeat_kv(k, r)), np.ascontiguousarray(_repeat_kv(v, r))
     if cu_seqlens_q is None:
         B, H, Sq, _ = q.shape
         outs = {"o": np.full((B, H, Sq, v.shape[3]), np.nan),
@@ -199,8 +237,13 @@ def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, of
         cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_dbias=None):
     """Backward definition (recomputes O and LSE itself).
 
-    Returns dict(o, lse, D, dq, dk, dv[, dbias])."""
+    Returns dict(o, lse, D, dq, dk, dv[, dbias]).  With fewer key/value heads
+    than query heads, dk and dv of key/value head hk are the sums of the
+    per-query-head gradients over its group (NaN for groups only partly in
+    `heads`)."""
     q, k, v, bias, dout = _as64(q), _as64(k), _as64(v), _as64(bias), _as64(dout)
+    r = _kv_ratio(q, k, cu_seqlens_q is not None)
+    k, v = np.ascontiguousarray(_repeat_kv(k, r)), np.ascontiguousarray(_repeat_kv(v, r))
     if want_dbias is None:
         want_dbias = bias is not None
     if cu_seqlens_q is None:
@@ -221,4 +264,15 @@ def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, of
     hs = _heads(q, k, v, bias, dout, outs, scale=scale, causal=causal, p_drop=p_drop,
                 seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads)
     _run("oracle_bwd", hs, threads)
+    if r > 1:
+        nb = q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1
+        sel = None if heads is None else set(heads)
+        def complete(hk):
+            return sel is None or all((b, hk * r + j) in sel for b in range(nb) for j in range(r))
+        if cu_seqlens_q is None:
+            outs["dk"] = _sum_groups(outs["dk"], r, complete)
+            outs["dv"] = _sum_groups(outs["dv"], r, complete)
+        else:  # [T, H, D]: heads on axis 1 as well
+            outs["dk"] = _sum_groups(outs["dk"], r, complete)
+            outs["dv"] = _sum_groups(outs["dv"], r, complete)
     return outs

@@ -263,6 +263,64 @@ def test_backward_matches_torch_autograd_float64(causal, with_bias, p):
         assert np.allclose(g["dbias"], tb.grad.numpy(), atol=1e-10, rtol=0)
 
 
+@pytest.mark.parametrize("hkv,causal,with_bias,p", [(1, True, False, 0.0), (2, False, True, 0.0),
+                                                     (2, True, False, 0.25)])
+def test_grouped_query_heads_match_torch_autograd_float64(hkv, causal, with_bias, p):
+    # grouped-query attention: query head h reads key/value head h // (H/hkv);
+    # torch composes it with index_select along heads, whose autograd sums
+    # the gradient over each group
+    B, H, Sq, Skv, Dq, Dv = 2, 4, 9, 12 if not causal else 9, 5, 3
+    q, dout = _rand((B, H, Sq, Dq), 60), _rand((B, H, Sq, Dv), 63)
+    k, v = _rand((B, hkv, Skv, Dq), 61), _rand((B, hkv, Skv, Dv), 62)
+    bias = _rand((B, H, Sq, Skv), 64) if with_bias else None
+    scale = 0.5
+    kw = dict(scale=scale, causal=causal, p_drop=p, seed=17, offset=4)
+    g = O.bwd(q, k, v, dout, bias=bias, **kw)
+    assert g["dk"].shape == k.shape and g["dv"].shape == v.shape
+    keep = O.fwd(q, k, v, bias=bias, want_keep=True, **kw)["keep"] if p > 0 else None
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    idx = torch.arange(H) // (H // hkv)
+    kk, vv = tk.index_select(1, idx), tv.index_select(1, idx)
+    s = scale * tq @ kk.transpose(-1, -2)
+    if with_bias:
+        s = s + torch.from_numpy(bias)
+    if causal:
+        s = s.masked_fill(~torch.ones(Sq, Skv, dtype=torch.bool).tril(), float("-inf"))
+    P = torch.softmax(s, -1)
+    if p > 0:
+        P = P * (torch.from_numpy(keep.astype(np.float64)) / (1.0 - np.float64(np.float32(p))))
+    out = P @ vv
+    out.backward(torch.from_numpy(dout))
+    assert np.allclose(g["o"], out.detach().numpy(), atol=1e-12, rtol=0)
+    assert np.allclose(g["dq"], tq.grad.numpy(), atol=1e-10, rtol=0)
+    assert np.allclose(g["dk"], tk.grad.numpy(), atol=1e-10, rtol=0)
+    assert np.allclose(g["dv"], tv.grad.numpy(), atol=1e-10, rtol=0)
+
+
+def test_grouped_query_heads_central_differences():
+    # MQA (one key/value head for three query heads), causal, on a tiny shape
+    B, H, S, Dq, Dv = 1, 3, 4, 3, 2
+    q, dout = _rand((B, H, S, Dq), 70), _rand((B, H, S, Dv), 73)
+    k, v = _rand((B, 1, S, Dq), 71), _rand((B, 1, S, Dv), 72)
+    kw = dict(scale=0.7, causal=True)
+    g = O.bwd(q, k, v, dout, **kw)
+    eps = 1e-6
+    for name, x in (("dk", k), ("dv", v), ("dq", q)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _loss(q, k, v, dout, None, **kw)
+            x[i] = old - eps
+            lm = _loss(q, k, v, dout, None, **kw)
+            x[i] = old
+            num[i] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(num - g[name])) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (name, err)
+
+
 @pytest.mark.parametrize("p", [0.0, 0.3])
 def test_backward_invariants(p):
     B, H, S, D = 1, 3, 29, 8
