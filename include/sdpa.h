@@ -87,6 +87,12 @@ typedef struct {
      * sequence length. */
     const int32_t *cu_seqlens_q;
     const int32_t *cu_seqlens_kv;
+    /* Key/value heads (grouped-query attention); 0 means h.  Must divide h.
+     * K, V, dK and dV have h_kv heads and query head i reads key/value head
+     * i / (h / h_kv) (Composable Kernel's i_nhead / nhead_ratio_qk; oneDNN's
+     * kv_group_size = h / h_kv).  dK and dV of a key/value head are the sums
+     * over its group of query heads, accumulated in a fixed order. */
+    int64_t h_kv;
 } sdpa_problem_t;
 
 /* Dropout keep mask (the library's own specification; the pages give the

@@ -63,6 +63,9 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
                 (double)p->dropout_probability);
   if (!std::isfinite(p->scaling_factor))
     return fail(SDPA_ERR_INVALID_ARG, "scaling_factor is not finite");
+  if (p->h_kv < 0 || (p->h_kv > 0 && p->h % p->h_kv != 0))
+    return fail(SDPA_ERR_INVALID_ARG, "h_kv=%lld must be 0 or divide h=%lld", (long long)p->h_kv,
+                (long long)p->h);
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
   if (p->dtype == SDPA_F32) {
@@ -78,6 +81,9 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
   }
   return SDPA_OK;
 }
+
+// query heads per key/value head
+int32_t kv_group(const sdpa_problem_t* p) { return p->h_kv > 0 ? (int32_t)(p->h / p->h_kv) : 1; }
 
 bool empty_problem(const sdpa_problem_t* p) {
   return p->b == 0 || p->h == 0 || p->s_q == 0 || p->s_kv == 0;
@@ -207,7 +213,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s);
   a.sb_ = to_str(bias_s); a.so_ = to_str(o_s);
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
-  a.B = (int32_t)p->b; a.H = (int32_t)p->h;
+  a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
@@ -224,7 +230,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
 }
 
 static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
-  a.B = (int32_t)p->b; a.H = (int32_t)p->h;
+  a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);

@@ -111,31 +111,32 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   const int w = wave_id();
   const int kb = w & 3;
   const bool roleA = w < 4;
-  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H, a.B, SDPA_DKDV_HEAD_GROUP);
+  // one workgroup per (batch, key/value head, key tile); it accumulates dK,
+  // dV over the query tiles of every query head of the head's group
+  const int G = a.G;
+  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H / G, a.B, SDPA_DKDV_HEAD_GROUP);
   if (!wi.valid) return;
-  const int b = wi.b, h = wi.h;
+  const int b = wi.b, hk = wi.h;
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
   const int kv0 = wi.tile * BC;  // causal: key tile 0 has the most query tiles
   if (kv0 >= skv) return;
 
-  const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
-  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
-  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
-  const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
-  const int64_t st_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
-  const uint16_t* bg = nullptr;
-  uint16_t* dbg = nullptr;
-  if (BIAS) {
-    bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
-    if (a.dbias) dbg = (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
-  }
+  const T* kg = base_ptr<T>(a.k, a.sk_, sp, hk, false);
+  const T* vg = base_ptr<T>(a.v, a.sv_, sp, hk, false);
+  // per query head: its bias / dBias rows
+  auto bias_head = [&](int h) __attribute__((always_inline)) {
+    return (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+  };
+  auto dbias_head = [&](int h) __attribute__((always_inline)) {
+    return (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
+  };
+  const bool want_dbias = BIAS && a.dbias != nullptr;
 
   const int wk0 = kv0 + 32 * kb;  // this wave's first key
   const int kvr = wk0 + l32;      // this lane's key
   const bool kv_ok = kvr < skv;
   DropKey dk{};
-  const uint32_t bh = (uint32_t)(b * a.H + h);
   if (DROP) dk = drop_key(a.drop);
   const float rescale = DROP ? a.drop.rescale : 1.f;
   const float c = a.scale_log2;
@@ -143,9 +144,26 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   // causal: query rows below kv0 see none of these keys
   const int q_begin = CAUSAL ? (kv0 / BQ) * BQ : 0;
   const int nq = sq > q_begin ? (sq - q_begin + BQ - 1) / BQ : 0;
-  if (CAUSAL && dbg && !roleA && kv_ok) {
+  // work items: item i is query tile i % nq of query head hk*G + i / nq,
+  // i < G * nq; the trip loop steps them incrementally (no divisions)
+  const int n_items = G * nq;
+  struct Item {
+    int h, q0;
+  };
+  auto next_item = [&](Item it) __attribute__((always_inline)) {
+    it.q0 += BQ;
+    if (it.q0 >= q_begin + nq * BQ) {
+      it.q0 = q_begin;
+      ++it.h;
+    }
+    return it;
+  };
+  if (CAUSAL && want_dbias && !roleA && kv_ok) {
     // dBias is zero wherever the mask hides the key: rows [0, q_begin)
-    for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+    for (int j = 0; j < G; ++j) {
+      uint16_t* dbg = dbias_head(hk * G + j);
+      for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+    }
   }
 
   // bias tiles come through LDS when the whole 32 x 128 tile is in range and
@@ -156,31 +174,41 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   TileLoader<DQK, BQ, T, NWQ> ldQ;
   TileLoader<DV, BQ, T, NWO> ldO;
   TileLoader<BC, BQ, T, 8> ldB;
-  if (w < NWQ) ldQ.init(qg, a.sq_.s, w, lane);
-  if (w < NWO) ldO.init(dog, a.sdo_.s, w, lane);
-  if (BIAS_LDS && bias_lds) ldB.init((const T*)(bg + kv0), a.sb_.s, w, lane);
-  auto issue = [&](int i) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ, set = i % NSET;
-    if (w < NWQ) ldQ.load(sQ[set], q0, sq, w, lane);
-    if (w < NWO) ldO.load(sO[set], q0, sq, w, lane);
-    if (BIAS_LDS && bias_lds) ldB.load(sB[set], q0, sq, w, lane);
+  // the loaders' per-lane offsets depend only on the row strides; the head
+  // of each item moves their base
+  if (w < NWQ) ldQ.init(base_ptr<T>(a.q, a.sq_, sp, hk * G, true), a.sq_.s, w, lane);
+  if (w < NWO) ldO.init(base_ptr<T>(a.dout, a.sdo_, sp, hk * G, true), a.sdo_.s, w, lane);
+  if (BIAS_LDS && bias_lds) ldB.init((const T*)(bias_head(hk * G) + kv0), a.sb_.s, w, lane);
+  auto issue = [&](int set, Item it) __attribute__((always_inline)) {
+    const int q0 = it.q0, h = it.h;
+    if (w < NWQ) {
+      ldQ.g = (const char*)base_ptr<T>(a.q, a.sq_, sp, h, true);
+      ldQ.load(sQ[set], q0, sq, w, lane);
+    }
+    if (w < NWO) {
+      ldO.g = (const char*)base_ptr<T>(a.dout, a.sdo_, sp, h, true);
+      ldO.load(sO[set], q0, sq, w, lane);
+    }
+    if (BIAS_LDS && bias_lds) {
+      ldB.g = (const char*)(bias_head(h) + kv0);
+      ldB.load(sB[set], q0, sq, w, lane);
+    }
     // the 32 LSE*log2(e) (wave 6) and D (wave 7) values, one row per lane,
     // rows clamped to the sequence
     if (w >= 6 && lane < BQ) {
       int r = q0 + lane;
       r = r < sq ? r : sq - 1;
+      const int64_t st_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
       const float* src = (w == 6 ? a.lse2 : a.dvec) + st_base + r;
       float* dst = w == 6 ? sL[set] : sD[set];
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
-  auto tile_active = [&](int i) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ;
-    return wk0 < skv && (!CAUSAL || q0 + BQ - 1 >= wk0);
+  auto tile_active = [&](Item it) __attribute__((always_inline)) {
+    return wk0 < skv && (!CAUSAL || it.q0 + BQ - 1 >= wk0);
   };
-  auto tile_needs_mask = [&](int i) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ;
-    return (q0 + BQ > sq) || (wk0 + 31 >= skv) || (CAUSAL && q0 < wk0 + 31);
+  auto tile_needs_mask = [&](Item it) __attribute__((always_inline)) {
+    return (it.q0 + BQ > sq) || (wk0 + 31 >= skv) || (CAUSAL && it.q0 < wk0 + 31);
   };
 
   RowReader<DQK, T> rdQ;
@@ -196,8 +224,11 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   constexpr uint32_t P_SLOT = 4 * 4 * 64 * 16;
 
   // ---- role A: S, P, dV for tile i -----------------------------------------
-  auto stepA = [&](int i, const u32x4* reg, f32x16* acc) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ, set = i % NSET;
+  auto stepA = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
+      __attribute__((always_inline)) {
+    const int q0 = it.q0, h = it.h;
+    const uint32_t bh = (uint32_t)(b * a.H + h);
+    const uint16_t* bg = BIAS ? bias_head(h) : nullptr;
     const auto vQ = rdQ.view(sQ[set]);
     const auto vOt = rdOt.view(sO[set]);
     // Operand reads issue in source order (their address XORs are volatile),
@@ -256,7 +287,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, x));
       }
     }
-    if (tile_needs_mask(i)) {
+    if (tile_needs_mask(it)) {
       keep_branch();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -302,8 +333,10 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   };
 
   // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
-  auto stepB = [&](int i, const u32x4* reg, f32x16* acc) __attribute__((always_inline)) {
-    const int q0 = q_begin + i * BQ, set = i % NSET;
+  auto stepB = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
+      __attribute__((always_inline)) {
+    const int q0 = it.q0;
+    uint16_t* dbg = want_dbias ? dbias_head(it.h) : nullptr;
     const auto vO = rdO.view(sO[set]);
     const auto vQt = rdQt.view(sQ[set]);
     // (in halves when the dK accumulator is large, to bound registers)
@@ -349,7 +382,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
           dpz = dp[r];
         }
         ds[e] = p * (dpz - Dq);
-        if (BIAS && dbg && kv_ok) {
+        if (want_dbias && kv_ok) {
           const int qr = q0 + lb + e;
           if (qr < sq) dbg[(int64_t)qr * a.sdb_.s + kvr] = (uint16_t)(pack2<T>(ds[e], 0.f) & 0xffffu);
         }
@@ -374,7 +407,8 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     }
   };
 
-  if (nq > 0) issue(0);
+  const Item first{hk * G, q_begin};
+  if (n_items > 0) issue(0, first);
   // Each role runs its own copy of the trip loop, so its stationary operands
   // and accumulators are sized for it alone; both copies meet the same
   // barriers.  Trip i: role A takes tile i, role B tile i - 1.
@@ -392,26 +426,36 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NA; ++j) acc[j] = f32x16{};
 
-    for (int i = 0; i <= nq; ++i) {
+    // items i - 1, i, i + 1 and their buffer sets, stepped each trip
+    Item prev{}, cur = first, nxt = next_item(first);
+    int set_prev = NSET - 1, set_cur = 0, set_nxt = 1;
+    for (int i = 0; i <= n_items; ++i) {
       wait_all();
-      __syncthreads();  // tile i landed; P(i-1) written; set (i+1)%3 free
-      if (i + 1 < nq) issue(i + 1);
+      __syncthreads();  // item i landed; P(i-1) written; set (i+1)%3 free
+      if (i + 1 < n_items) issue(set_nxt, nxt);
       if constexpr (IS_A) {
-        if (i < nq && tile_active(i)) stepA(i, reg, acc);
+        if (i < n_items && tile_active(cur)) stepA(i, set_cur, cur, reg, acc);
       } else if (i >= 1) {
-        if (tile_active(i - 1)) {
-          stepB(i - 1, reg, acc);
-        } else if (CAUSAL && dbg && kv_ok) {
-          const int q0 = q_begin + (i - 1) * BQ;  // the whole tile is hidden from my key
-          for (int r = q0 + g; r < min(q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+        if (tile_active(prev)) {
+          stepB(i - 1, set_prev, prev, reg, acc);
+        } else if (CAUSAL && want_dbias && kv_ok) {
+          // the whole tile is hidden from my key
+          uint16_t* dbg = dbias_head(prev.h);
+          for (int r = prev.q0 + g; r < min(prev.q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
         }
       }
+      prev = cur;
+      cur = nxt;
+      nxt = next_item(nxt);
+      set_prev = set_cur;
+      set_cur = set_nxt;
+      set_nxt = set_nxt == NSET - 1 ? 0 : set_nxt + 1;
     }
 
     // epilogue: dV = rescale * dV^T acc (role A), dK = scale * dK^T acc (role B)
     if (kv_ok) {
-      T* dst = IS_A ? base_ptr_mut<T>(a.dv, a.sdv_, sp, h, false) + (int64_t)kvr * a.sdv_.s
-                    : base_ptr_mut<T>(a.dk, a.sdk_, sp, h, false) + (int64_t)kvr * a.sdk_.s;
+      T* dst = IS_A ? base_ptr_mut<T>(a.dv, a.sdv_, sp, hk, false) + (int64_t)kvr * a.sdv_.s
+                    : base_ptr_mut<T>(a.dk, a.sdk_, sp, hk, false) + (int64_t)kvr * a.sdk_.s;
       const float f = IS_A ? rescale : a.scale;
 #pragma unroll
       for (int db = 0; db < NA; ++db) {
@@ -464,8 +508,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   if (q0 >= sq) return;
 
   const T* qg = base_ptr<T>(a.q, a.sq_, sp, h, true);
-  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h, false);
-  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h, false);
+  const T* kg = base_ptr<T>(a.k, a.sk_, sp, h / a.G, false);
+  const T* vg = base_ptr<T>(a.v, a.sv_, sp, h / a.G, false);
   const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
@@ -682,8 +726,8 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
   if (i >= sp.sq) return;
   const float* qi = base_ptr<float>(a.q, a.sq_, sp, h, true) + (int64_t)i * a.sq_.s;
   const float* doi = base_ptr<float>(a.dout, a.sdo_, sp, h, true) + (int64_t)i * a.sdo_.s;
-  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h, false);
-  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h, false);
+  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h / a.G, false);
+  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h / a.G, false);
   const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
                                  (int64_t)i * a.sb_.s
                            : nullptr;
@@ -736,21 +780,14 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
 template <bool CAUSAL, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int b = blockIdx.z, hk = blockIdx.y;  // key/value head
   const SeqPos sp = resolve_seq(a.seq, b);
   const int j = blockIdx.x * 4 + w;
   if (j >= sp.skv) return;
-  const float* kj = base_ptr<float>(a.k, a.sk_, sp, h, false) + (int64_t)j * a.sk_.s;
-  const float* vj = base_ptr<float>(a.v, a.sv_, sp, h, false) + (int64_t)j * a.sv_.s;
-  const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true);
-  const float* dog = base_ptr<float>(a.dout, a.sdo_, sp, h, true);
-  const float* bcol = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h + j : nullptr;
-  float* dbcol = (BIAS && a.dbias) ? (float*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h + j
-                                   : nullptr;
+  const float* kj = base_ptr<float>(a.k, a.sk_, sp, hk, false) + (int64_t)j * a.sk_.s;
+  const float* vj = base_ptr<float>(a.v, a.sv_, sp, hk, false) + (int64_t)j * a.sv_.s;
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
-  const uint32_t bh = (uint32_t)(b * a.H + h);
-  const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
   float k[4], v[4], gk[4], gv[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -761,34 +798,46 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
     gv[c] = 0.f;
   }
   const int i0 = CAUSAL ? min(j, sp.sq) : 0;
-  if (dbcol && lane == 0)
-    for (int i = 0; i < i0; ++i) dbcol[(int64_t)i * a.sdb_.s] = 0.f;
-  for (int i = i0; i < sp.sq; ++i) {
-    const float* qi = qg + (int64_t)i * a.sq_.s;
-    const float* doi = dog + (int64_t)i * a.sdo_.s;
-    float ps = 0.f, pd = 0.f;
+  // the query heads of this key/value head's group, in ascending order
+  for (int h = hk * a.G; h < (hk + 1) * a.G; ++h) {
+    const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true);
+    const float* dog = base_ptr<float>(a.dout, a.sdo_, sp, h, true);
+    const float* bcol =
+        BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h + j : nullptr;
+    float* dbcol = (BIAS && a.dbias)
+                       ? (float*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h + j
+                       : nullptr;
+    const uint32_t bh = (uint32_t)(b * a.H + h);
+    const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
+    if (dbcol && lane == 0)
+      for (int i = 0; i < i0; ++i) dbcol[(int64_t)i * a.sdb_.s] = 0.f;
+    for (int i = i0; i < sp.sq; ++i) {
+      const float* qi = qg + (int64_t)i * a.sq_.s;
+      const float* doi = dog + (int64_t)i * a.sdo_.s;
+      float ps = 0.f, pd = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int d = lane + 64 * c;
-      if (d < dqk) ps += qi[d] * k[c];
-      if (d < dv) pd += doi[d] * v[c];
-    }
-    float s = wave_sum(ps) * a.scale + (BIAS ? bcol[(int64_t)i * a.sb_.s] : 0.f);
-    float dp = wave_sum(pd);
-    float p = exp2f(s * kLog2e - a.lse2[d_base + i]);
-    float z = 1.f;
-    if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
-    float ds = p * (dp * z - a.dvec[d_base + i]);
-    if (dbcol && lane == 0) dbcol[(int64_t)i * a.sdb_.s] = ds;
+      for (int c = 0; c < 4; ++c) {
+        int d = lane + 64 * c;
+        if (d < dqk) ps += qi[d] * k[c];
+        if (d < dv) pd += doi[d] * v[c];
+      }
+      float s = wave_sum(ps) * a.scale + (BIAS ? bcol[(int64_t)i * a.sb_.s] : 0.f);
+      float dp = wave_sum(pd);
+      float p = exp2f(s * kLog2e - a.lse2[d_base + i]);
+      float z = 1.f;
+      if (DROP) z = keep_one(dk, bh, i, j) ? a.drop.rescale : 0.f;
+      float ds = p * (dp * z - a.dvec[d_base + i]);
+      if (dbcol && lane == 0) dbcol[(int64_t)i * a.sdb_.s] = ds;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int d = lane + 64 * c;
-      if (d < dqk) gk[c] += ds * qi[d];
-      if (d < dv) gv[c] += p * z * doi[d];
+      for (int c = 0; c < 4; ++c) {
+        int d = lane + 64 * c;
+        if (d < dqk) gk[c] += ds * qi[d];
+        if (d < dv) gv[c] += p * z * doi[d];
+      }
     }
   }
-  float* dkj = base_ptr_mut<float>(a.dk, a.sdk_, sp, h, false) + (int64_t)j * a.sdk_.s;
-  float* dvj = base_ptr_mut<float>(a.dv, a.sdv_, sp, h, false) + (int64_t)j * a.sdv_.s;
+  float* dkj = base_ptr_mut<float>(a.dk, a.sdk_, sp, hk, false) + (int64_t)j * a.sdk_.s;
+  float* dvj = base_ptr_mut<float>(a.dv, a.sdv_, sp, hk, false) + (int64_t)j * a.sdv_.s;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     int d = lane + 64 * c;
@@ -818,7 +867,7 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
 
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
-  dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H, a.B), block(512);
+  dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H / a.G, a.B), block(512);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)
 #undef L
@@ -860,7 +909,7 @@ hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs
   const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
   if (t == IoType::BF16) return dkdv_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
   if (t == IoType::F16) return dkdv_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
-  dim3 grid((a.seq.s_kv + 3) / 4, a.H, a.B), block(256);
+  dim3 grid((a.seq.s_kv + 3) / 4, a.H / a.G, a.B), block(256);
 #define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
   SDPA_FLAG_SWITCH(L)
 #undef L

@@ -73,8 +73,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 
   TileLoader<DQK, BC, T> ldK;
   TileLoader<DV, BC, T> ldV;
-  ldK.init(base_ptr<T>(a.k, a.sk_, sp, h, false), a.sk_.s, w, lane);
-  ldV.init(base_ptr<T>(a.v, a.sv_, sp, h, false), a.sv_.s, w, lane);
+  ldK.init(base_ptr<T>(a.k, a.sk_, sp, h / a.G, false), a.sk_.s, w, lane);
+  ldV.init(base_ptr<T>(a.v, a.sv_, sp, h / a.G, false), a.sv_.s, w, lane);
   if (nt > 0) {
     ldK.load(sK[0], 0, skv, w, lane);
     ldV.load(sV[0], 0, skv, w, lane);
@@ -331,8 +331,8 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
   const int row = blockIdx.x * 4 + w;
   if (row >= sp.sq) return;
   const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true) + (int64_t)row * a.sq_.s;
-  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h, false);
-  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h, false);
+  const float* kg = base_ptr<float>(a.k, a.sk_, sp, h / a.G, false);
+  const float* vg = base_ptr<float>(a.v, a.sv_, sp, h / a.G, false);
   float* og = base_ptr_mut<float>(a.o, a.so_, sp, h, true) + (int64_t)row * a.so_.s;
   const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
                                  (int64_t)row * a.sb_.s

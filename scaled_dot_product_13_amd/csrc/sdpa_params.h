@@ -39,6 +39,7 @@ struct FwdArgs {
   Str sq_, sk_, sv_, sb_, so_;
   int32_t bias_vec;  // bias rows 16-byte aligned: vector loads allowed
   int32_t B, H;
+  int32_t G;           // query heads per key/value head (K/V head of h is h / G)
   SeqInfo seq;
   float scale;         // scaling_factor
   float scale_log2;    // scaling_factor * log2(e)
@@ -56,6 +57,7 @@ struct BwdArgs {
   Str sq_, sk_, sv_, sb_, so_, sdo_, sdq_, sdk_, sdv_, sdb_;
   int32_t bias_vec;
   int32_t B, H;
+  int32_t G;  // query heads per key/value head (K/V head of h is h / G)
   SeqInfo seq;
   float scale, scale_log2;
   DropoutArgs drop;

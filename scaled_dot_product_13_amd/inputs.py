@@ -37,6 +37,7 @@ class Workload:
     # group (varlen) mode: number of sequences and the length range
     varlen: Optional[tuple] = None  # (n_seq, lo, hi)
     scale: Optional[float] = None
+    h_kv: Optional[int] = None  # key/value heads (grouped-query); None = h
     extra: dict = field(default_factory=dict)
 
     @property
@@ -73,14 +74,16 @@ def make_inputs(wl: Workload, lengths=None):
         cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
         cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
         T = int(cu[-1])
-        shp_q, shp_k, shp_v, shp_o = (T, wl.h, wl.d_qk), (T, wl.h, wl.d_qk), (T, wl.h, wl.d_v), (T, wl.h, wl.d_v)
+        hk = wl.h_kv or wl.h
+        shp_q, shp_k, shp_v, shp_o = (T, wl.h, wl.d_qk), (T, hk, wl.d_qk), (T, hk, wl.d_v), (T, wl.h, wl.d_v)
         out["lengths"] = lengths
         out["cu_seqlens"] = cu
         out["max_seqlen"] = int(lengths.max()) if len(lengths) else 0
     else:
+        hk = wl.h_kv or wl.h
         shp_q = (wl.b, wl.h, wl.s_q, wl.d_qk)
-        shp_k = (wl.b, wl.h, wl.s_kv, wl.d_qk)
-        shp_v = (wl.b, wl.h, wl.s_kv, wl.d_v)
+        shp_k = (wl.b, hk, wl.s_kv, wl.d_qk)
+        shp_v = (wl.b, hk, wl.s_kv, wl.d_v)
         shp_o = (wl.b, wl.h, wl.s_q, wl.d_v)
     out["q"] = torch.randn(shp_q, generator=g, dtype=torch.float32).to(io)
     out["k"] = torch.randn(shp_k, generator=g, dtype=torch.float32).to(io)
@@ -93,7 +96,7 @@ def make_inputs(wl: Workload, lengths=None):
 
 
 def small(dtype="bf16", b=1, h=2, s_q=200, s_kv=200, d_qk=128, d_v=128, causal=False,
-          bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None) -> Workload:
+          bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None, h_kv=None) -> Workload:
     """A small workload (parity-test size) with the same recipe."""
     return Workload(f"small-{dtype}", dtype, b, h, s_q, s_kv, d_qk, d_v, causal=causal, bias=bias,
-                    dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale)
+                    dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale, h_kv=h_kv)

@@ -44,6 +44,7 @@ class Problem(ctypes.Structure):
         ("dropout_seed", ctypes.c_uint64), ("dropout_offset", ctypes.c_uint64),
         ("dropout_seed_offset_dev", ctypes.c_void_p),
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
+        ("h_kv", ctypes.c_int64),
     ]
 
 
@@ -128,7 +129,8 @@ def _stream():
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None):
-    """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group [T,H,D])."""
+    """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group
+    [T,H,D]); k and v may have fewer heads than q (grouped-query attention)."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     group = cu_seqlens_q is not None
@@ -146,6 +148,7 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     else:
         p.b, p.h, p.s_q, p.d_qk = q.shape
         p.s_kv, p.d_v = k.shape[2], v.shape[3]
+    p.h_kv = k.shape[1]
     p.scaling_factor = float(scale if scale is not None else 1.0 / math.sqrt(p.d_qk))
     p.is_causal = 1 if causal else 0
     p.dropout_probability = float(dropout_p)

@@ -53,6 +53,7 @@ def _problem(S, **kw):
         p.cu_seqlens_q = kw["cu_q"]
     if "cu_kv" in kw:
         p.cu_seqlens_kv = kw["cu_kv"]
+    p.h_kv = kw.get("hkv", 0)
     return p
 
 
@@ -95,6 +96,11 @@ def test_invalid_arguments(S):
     assert _fwd(S, _problem(S), q=None) == S.SDPA_ERR_INVALID_ARG
     assert b"q is null" in L.sdpa_last_error_message()
     assert _fwd(S, _problem(S), st=S.Strides(-1, 128, 128)) == S.SDPA_ERR_INVALID_ARG
+    # key/value heads must divide the query heads (0 = as many as query heads)
+    assert _fwd(S, _problem(S, h=4, hkv=3)) == S.SDPA_ERR_INVALID_ARG
+    assert b"h_kv" in L.sdpa_last_error_message()
+    assert _fwd(S, _problem(S, h=4, hkv=-1)) == S.SDPA_ERR_INVALID_ARG
+    assert _bwd(S, _problem(S, h=6, hkv=4)) == S.SDPA_ERR_INVALID_ARG
 
 
 def test_unsupported_combinations(S):

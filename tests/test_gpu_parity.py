@@ -117,17 +117,31 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
     got = {"o": o, "dq": dq, "dk": dk, "dv": dv}
     if dbias is not None:
         got["dbias"] = dbias
+    # grouped-query: dK, dV have one head per group of r query heads; compare
+    # them once per key/value head whose whole group is among `heads`
+    r = wl.h // (wl.h_kv or wl.h)
+    hset = set(heads)
+    def head_of(name, b, h):
+        if name not in ("dk", "dv"):
+            return h
+        if h % r != 0 or any((b, h + j) not in hset for j in range(r)):
+            return None
+        return h // r
     for (b, h) in heads:
         if group:
             c0, c1 = int(x["cu_seqlens"][b]), int(x["cu_seqlens"][b + 1])
             sl = slice(c0, c1)
             for name, t in got.items():
-                errs[name] = max(errs.get(name, 0), _cmp(name, _np(t[sl, h]), ref[name][sl, h], x["dtype"]))
+                hh = head_of(name, b, h)
+                if hh is not None:
+                    errs[name] = max(errs.get(name, 0), _cmp(name, _np(t[sl, hh]), ref[name][sl, hh], x["dtype"]))
             errs["lse"] = max(errs.get("lse", 0), _cmp("lse", _np(lse[h, sl]), ref["lse"][h, sl], x["dtype"]))
         else:
             dD = np.sum(dout[b, h].double().numpy() * (_np(o[b, h]) - ref["o"][b, h]), -1)
             for name, t in got.items():
-                errs[name] = max(errs.get(name, 0), _cmp(name, _np(t[b, h]), ref[name][b, h], x["dtype"], dD))
+                hh = head_of(name, b, h)
+                if hh is not None:
+                    errs[name] = max(errs.get(name, 0), _cmp(name, _np(t[b, hh]), ref[name][b, hh], x["dtype"], dD))
             errs["lse"] = max(errs.get("lse", 0), _cmp("lse", _np(lse[b, h]), ref["lse"][b, h], x["dtype"]))
             if want_keep:
                 gk_ = keep[b, h].cpu().numpy()
@@ -160,6 +174,32 @@ SMALL = [
     ("f32", (64, 64), 77, 90, True, True, 0.1),
     ("f32", (128, 32), 33, 65, False, False, 0.0),
 ]
+
+
+GQA = [
+    # dtype, dims, s_q, s_kv, causal, bias, p, h, h_kv
+    ("bf16", (128, 128), 200, 200, True, False, 0.0, 4, 2),
+    ("bf16", (128, 128), 130, 260, False, False, 0.0, 4, 1),
+    ("f16", (64, 64), 150, 150, True, True, 0.1, 6, 2),
+    ("f16", (192, 128), 96, 200, False, True, 0.0, 4, 2),
+    ("f32", (64, 64), 70, 90, True, False, 0.1, 4, 2),
+]
+
+
+@pytest.mark.parametrize("case", GQA, ids=lambda c: f"{c[0]}-d{c[1][0]}-h{c[7]}kv{c[8]}-c{int(c[4])}"
+                         f"-b{int(c[5])}-p{c[6]}")
+def test_grouped_query_parity(S, case):
+    dt, (dq_, dv_), sq, skv, causal, bias, p, h, hkv = case
+    wl = inputs.small(dt, b=2, h=h, s_q=sq, s_kv=skv, d_qk=dq_, d_v=dv_, causal=causal, bias=bias,
+                      dropout_p=p, seed=sq * 5 + skv + h, h_kv=hkv)
+    run_workload(S, wl)
+
+
+def test_grouped_query_varlen(S):
+    lengths = [100, 1, 257, 64]
+    wl = inputs.small("bf16", b=len(lengths), h=4, h_kv=2, d_qk=128, d_v=128, causal=True, seed=91,
+                      varlen=(len(lengths), 1, 257))
+    run_workload(S, wl, lengths=lengths)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
