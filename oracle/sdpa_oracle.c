@@ -28,6 +28,12 @@
  *   - "causal" is the top-left mask: j is visible from i iff j <= i (the
  *     oneDNN micro SDPA host driver, init_conf_common, names both top-left and
  *     bottom-right kinds; the CK mask object is built with a top-left flag).
+ *   - The general mask is a band around the diagonal (CK builds its mask
+ *     from a left / right window and the top-left flag, in
+ *     FmhaBwdDQDKDVKernel's operator()): j is visible from i iff
+ *     lo <= j - i - off <= hi, with off = 0 (top-left) or s_kv - s_q
+ *     (bottom-right), lo = -window_left and hi = window_right (either side
+ *     unbounded when not given), and causal meaning hi <= 0.
  *   - A row with no visible key has O_i = 0, LSE_i = -inf and zero gradients
  *     (oneDNN's softmax_inf_as_zero flag).
  *   - Dropout multiplies the normalised P after the row statistics are taken;
@@ -124,61 +130,79 @@ typedef struct {
     int64_t ld_o, ld_dq, ld_dk, ld_dv, ld_dbias;
     uint8_t *keep; /* optional [sq][skv] keep bits (allowed (i,j) only) */
     int64_t ld_keep;
+    /* General band mask (when band != 0; `causal` is then ignored): key j is
+     * visible from row i iff band_lo <= j - i - band_off <= band_hi.
+     * band_off = s_kv - s_q aligns the diagonal to the bottom-right corner,
+     * 0 to the top-left; band_lo / band_hi bound a sliding window (CK's
+     * window_size_left/right with its top-left / bottom-right mask kinds,
+     * oneDNN's top-left and bottom-right causal kinds). */
+    int32_t band;
+    int64_t band_off, band_lo, band_hi;
 } oracle_head_t;
 
-/* last key index visible from row i, or -1 if none (top-left causal) */
-static int64_t last_visible(const oracle_head_t *h, int64_t i) {
-    int64_t last = h->skv - 1;
-    if (h->causal && i < last) last = i;
-    return last;
+/* Visible keys of row i: the contiguous range [*first, *last]; empty when
+ * *first > *last.  Without a band: all keys, or top-left causal j <= i. */
+static void visible_range(const oracle_head_t *h, int64_t i, int64_t *first, int64_t *last) {
+    int64_t f = 0, l = h->skv - 1;
+    if (h->band) {
+        int64_t lo = i + h->band_off + h->band_lo, hi = i + h->band_off + h->band_hi;
+        if (lo > f) f = lo;
+        if (hi < l) l = hi;
+    } else if (h->causal && i < l) {
+        l = i;
+    }
+    *first = f;
+    *last = l;
 }
 
 /* Row i of the forward: fills s[0..last] with P_ij (probabilities, undropped)
  * and returns LSE_i.  Returns -inf and leaves s untouched if no key is visible. */
 static double row_probs(const oracle_head_t *h, int64_t i, double *s) {
-    int64_t last = last_visible(h, i);
-    if (last < 0) return -INFINITY;
+    int64_t first, last;
+    visible_range(h, i, &first, &last);
+    if (first > last) return -INFINITY;
     const double *qi = h->q + i * h->ld_q;
-    for (int64_t j = 0; j <= last; ++j) {
+    for (int64_t j = first; j <= last; ++j) {
         const double *kj = h->k + j * h->ld_k;
         double acc = 0.0;
         for (int64_t c = 0; c < h->dqk; ++c) acc += qi[c] * kj[c];
         s[j] = h->scale * acc + (h->bias ? h->bias[i * h->ld_bias + j] : 0.0);
     }
     double m = -INFINITY;
-    for (int64_t j = 0; j <= last; ++j)
+    for (int64_t j = first; j <= last; ++j)
         if (s[j] > m) m = s[j];
     double l = 0.0;
-    for (int64_t j = 0; j <= last; ++j) l += exp(s[j] - m);
-    for (int64_t j = 0; j <= last; ++j) s[j] = exp(s[j] - m) / l;
+    for (int64_t j = first; j <= last; ++j) l += exp(s[j] - m);
+    for (int64_t j = first; j <= last; ++j) s[j] = exp(s[j] - m) / l;
     return m + log(l);
 }
 
 /* Z_ij for the visible keys of row i (1 everywhere when p == 0). */
-static void row_dropout(const oracle_head_t *h, int64_t i, int64_t last, double *z) {
+static void row_dropout(const oracle_head_t *h, int64_t i, int64_t first, int64_t last, double *z) {
     if (h->p_drop <= 0.0f) {
-        for (int64_t j = 0; j <= last; ++j) z[j] = 1.0;
+        for (int64_t j = first; j <= last; ++j) z[j] = 1.0;
         return;
     }
     int thr = oracle_drop_threshold(h->p_drop);
     double rescale = 1.0 / (1.0 - (double)h->p_drop);
-    for (int64_t j = 0; j <= last; ++j)
+    for (int64_t j = first; j <= last; ++j)
         z[j] = oracle_keep_bit(h->seed, h->offset, h->bh, i, j, thr) ? rescale : 0.0;
 }
 
 static void head_fwd(const oracle_head_t *h, double *s, double *z) {
     for (int64_t i = 0; i < h->sq; ++i) {
         double *oi = h->o + i * h->ld_o;
-        int64_t last = last_visible(h, i);
+        int64_t first, last;
+        visible_range(h, i, &first, &last);
         double lse = row_probs(h, i, s);
         if (h->lse) h->lse[i] = lse;
         for (int64_t e = 0; e < h->dv; ++e) oi[e] = 0.0;
-        if (last < 0) continue;
-        row_dropout(h, i, last, z);
+        if (first > last) continue;
+        row_dropout(h, i, first, last, z);
         if (h->keep)
-            for (int64_t j = 0; j <= last; ++j)
+            for (int64_t j = first; j <= last; ++j)
                 h->keep[i * h->ld_keep + j] = z[j] != 0.0;
-        for (int64_t j = 0; j <= last; ++j) {
+        for (int64_t j = first; j <= last; ++j) {
             const double *vj = h->v + j * h->ld_v;
             double w = s[j] * z[j];
             for (int64_t e = 0; e < h->dv; ++e) oi[e] += w * vj[e];
@@ -198,18 +222,19 @@ static void head_bwd(const oracle_head_t *h, double *s, double *z, double *oi) {
         for (int64_t c = 0; c < h->dqk; ++c) dqi[c] = 0.0;
         if (h->dbias)
             for (int64_t j = 0; j < h->skv; ++j) h->dbias[i * h->ld_dbias + j] = 0.0;
-        int64_t last = last_visible(h, i);
+        int64_t first, last;
+        visible_range(h, i, &first, &last);
         double lse = row_probs(h, i, s);
-        if (last < 0) {
+        if (first > last) {
             if (h->dvec) h->dvec[i] = 0.0;
             if (h->o) for (int64_t e = 0; e < h->dv; ++e) h->o[i * h->ld_o + e] = 0.0;
             if (h->lse) h->lse[i] = lse;
             continue;
         }
-        row_dropout(h, i, last, z);
+        row_dropout(h, i, first, last, z);
         /* O_i from this oracle's own forward definition */
         for (int64_t e = 0; e < h->dv; ++e) oi[e] = 0.0;
-        for (int64_t j = 0; j <= last; ++j) {
+        for (int64_t j = first; j <= last; ++j) {
             const double *vj = h->v + j * h->ld_v;
             double w = s[j] * z[j];
             for (int64_t e = 0; e < h->dv; ++e) oi[e] += w * vj[e];
@@ -221,7 +246,7 @@ static void head_bwd(const oracle_head_t *h, double *s, double *z, double *oi) {
         if (h->o) for (int64_t e = 0; e < h->dv; ++e) h->o[i * h->ld_o + e] = oi[e];
         if (h->lse) h->lse[i] = lse;
         const double *qi = h->q + i * h->ld_q;
-        for (int64_t j = 0; j <= last; ++j) {
+        for (int64_t j = first; j <= last; ++j) {
             const double *vj = h->v + j * h->ld_v;
             const double *kj = h->k + j * h->ld_k;
             double pz = s[j] * z[j];

@@ -45,6 +45,8 @@ class _Head(ctypes.Structure):
         ("ld_dk", ctypes.c_int64), ("ld_dv", ctypes.c_int64),
         ("ld_dbias", ctypes.c_int64),
         ("keep", ctypes.POINTER(ctypes.c_uint8)), ("ld_keep", ctypes.c_int64),
+        ("band", ctypes.c_int32), ("band_off", ctypes.c_int64),
+        ("band_lo", ctypes.c_int64), ("band_hi", ctypes.c_int64),
     ]
 
 
@@ -101,8 +103,23 @@ def _as64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+_UNBOUNDED = 1 << 62
+
+
+def _band(causal, bottom_right, window_left, window_right):
+    """(lo, hi) of the visible band j - i - off, or None for the plain
+    (unmasked or top-left causal) cases."""
+    if not bottom_right and window_left is None and window_right is None:
+        return None
+    lo = -int(window_left) if window_left is not None else -_UNBOUNDED
+    hi = int(window_right) if window_right is not None else _UNBOUNDED
+    if causal:
+        hi = min(hi, 0)
+    return lo, hi
+
+
 def _heads(q, k, v, bias, dout, outs, *, scale, causal, p_drop, seed, offset,
-           cu_q, cu_kv, select):
+           cu_q, cu_kv, select, band=None, bottom_right=False):
     """Build the list of head descriptors for batch or varlen layout."""
     heads = []
     keep = outs.get("keep")
@@ -163,6 +180,10 @@ def _heads(q, k, v, bias, dout, outs, *, scale, causal, p_drop, seed, offset,
     for hd in heads:
         hd.scale = float(scale)
         hd.causal = 1 if causal else 0
+        if band is not None:
+            hd.band = 1
+            hd.band_off = hd.skv - hd.sq if bottom_right else 0
+            hd.band_lo, hd.band_hi = band
         hd.p_drop = float(p_drop)
         hd.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
         hd.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
@@ -210,9 +231,12 @@ def _sum_groups(t, r, complete):
 
 
 def fwd(q, k, v, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0,
-        cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_keep=False):
+        cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_keep=False,
+        bottom_right=False, window_left=None, window_right=None):
     """Forward definition.  Returns dict(o=..., lse=..., [keep=...]).
-    k and v may have fewer heads than q (grouped-query attention)."""
+    k and v may have fewer heads than q (grouped-query attention).  The mask
+    is top-left causal, or with bottom_right / window_left / window_right the
+    band lo <= j - i - off <= hi described in the C source."""
     q, k, v, bias = _as64(q), _as64(k), _as64(v), _as64(bias)
     r = _kv_ratio(q, k, cu_seqlens_q is not None)
     k, v = np.ascontiguousarray(_repeat_kv(k, r)), np.ascontiguousarray(_repeat_kv(v, r))
@@ -228,13 +252,16 @@ def fwd(q, k, v, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0
         outs = {"o": np.full((Tq, H, v.shape[2]), np.nan),
                 "lse": np.full((H, Tq), np.nan)}
     hs = _heads(q, k, v, bias, None, outs, scale=scale, causal=causal, p_drop=p_drop,
-                seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads)
+                seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads,
+                band=_band(causal, bottom_right, window_left, window_right),
+                bottom_right=bottom_right)
     _run("oracle_fwd", hs, threads)
     return outs
 
 
 def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0,
-        cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_dbias=None):
+        cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_dbias=None,
+        bottom_right=False, window_left=None, window_right=None):
     """Backward definition (recomputes O and LSE itself).
 
     Returns dict(o, lse, D, dq, dk, dv[, dbias]).  With fewer key/value heads
@@ -262,7 +289,9 @@ def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, of
                 "dq": np.full(q.shape, np.nan), "dk": np.full(k.shape, np.nan),
                 "dv": np.full(v.shape, np.nan)}
     hs = _heads(q, k, v, bias, dout, outs, scale=scale, causal=causal, p_drop=p_drop,
-                seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads)
+                seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads,
+                band=_band(causal, bottom_right, window_left, window_right),
+                bottom_right=bottom_right)
     _run("oracle_bwd", hs, threads)
     if r > 1:
         nb = q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1

@@ -321,6 +321,91 @@ def test_grouped_query_heads_central_differences():
         assert err < 1e-6, (name, err)
 
 
+# ------------------------------------------------------------ band masks ----
+def test_bottom_right_causal_is_top_left_when_square():
+    q, k, v = _rand((1, 2, 9, 4), 80), _rand((1, 2, 9, 4), 81), _rand((1, 2, 9, 3), 82)
+    a = O.fwd(q, k, v, scale=0.5, causal=True)
+    b = O.fwd(q, k, v, scale=0.5, causal=True, bottom_right=True)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_bottom_right_causal_equals_last_rows_of_a_longer_query():
+    # Rows are independent: bottom-right alignment of s_q queries against
+    # s_kv keys is top-left causal attention of a query sequence extended to
+    # s_kv rows (any values in the extra leading rows), keeping the last s_q.
+    Sq, Skv = 5, 11
+    q, k, v = _rand((1, 2, Sq, 4), 83), _rand((1, 2, Skv, 4), 84), _rand((1, 2, Skv, 3), 85)
+    qq = np.concatenate([_rand((1, 2, Skv - Sq, 4), 86), q], axis=2)
+    a = O.fwd(q, k, v, scale=0.6, causal=True, bottom_right=True)
+    b = O.fwd(qq, k, v, scale=0.6, causal=True)
+    assert np.allclose(a["o"], b["o"][:, :, Skv - Sq:], atol=1e-12, rtol=0)
+    assert np.allclose(a["lse"], b["lse"][:, :, Skv - Sq:], atol=1e-12, rtol=0)
+
+
+def test_bottom_right_rows_without_keys():
+    # s_q > s_kv: the first s_q - s_kv rows see no key (O = 0, LSE = -inf, no gradient)
+    Sq, Skv = 7, 4
+    q, do = _rand((1, 1, Sq, 3), 87), _rand((1, 1, Sq, 2), 88)
+    k, v = _rand((1, 1, Skv, 3), 89), _rand((1, 1, Skv, 2), 90)
+    g = O.bwd(q, k, v, do, scale=0.5, causal=True, bottom_right=True)
+    n = Sq - Skv
+    assert np.all(g["o"][0, 0, :n] == 0) and np.all(np.isneginf(g["lse"][0, 0, :n]))
+    assert np.all(g["dq"][0, 0, :n] == 0)
+    assert np.isfinite(g["lse"][0, 0, n:]).all()
+
+
+@pytest.mark.parametrize("wl,wr,causal", [(2, None, True), (1, 2, False), (0, 0, False),
+                                          (None, 1, False)])
+def test_sliding_window_rows_are_softmax_over_their_key_slice(wl, wr, causal):
+    # each row's output is plain softmax attention over exactly the keys in
+    # its window, computed row by row with torch on the sliced K, V
+    Sq, Skv, scale = 8, 8, 0.7
+    q, k, v = _rand((1, 1, Sq, 4), 91), _rand((1, 1, Skv, 4), 92), _rand((1, 1, Skv, 3), 93)
+    r = O.fwd(q, k, v, scale=scale, causal=causal, window_left=wl, window_right=wr)
+    for i in range(Sq):
+        lo = 0 if wl is None else max(0, i - wl)
+        hi = Skv - 1 if wr is None else min(Skv - 1, i + wr)
+        if causal:
+            hi = min(hi, i)
+        tq = torch.from_numpy(q[0, 0, i:i + 1])
+        tk, tv = torch.from_numpy(k[0, 0, lo:hi + 1]), torch.from_numpy(v[0, 0, lo:hi + 1])
+        s = scale * tq @ tk.T
+        assert np.allclose(r["o"][0, 0, i], (torch.softmax(s, -1) @ tv).numpy()[0], atol=1e-12, rtol=0)
+        assert np.isclose(r["lse"][0, 0, i], torch.logsumexp(s, -1).item(), atol=1e-12, rtol=0)
+
+
+def test_unbounded_window_is_the_plain_mask():
+    q, k, v = _rand((1, 2, 9, 4), 94), _rand((1, 2, 12, 4), 95), _rand((1, 2, 12, 3), 96)
+    a = O.fwd(q, k, v, scale=0.5, causal=True)
+    b = O.fwd(q, k, v, scale=0.5, causal=True, window_left=100)
+    c = O.fwd(q, k, v, scale=0.5)
+    d = O.fwd(q, k, v, scale=0.5, window_left=50, window_right=50)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(c["o"], d["o"])
+
+
+def test_band_backward_central_differences():
+    B, H, Sq, Skv, Dq, Dv = 1, 1, 5, 7, 3, 2
+    q, k, v = _rand((B, H, Sq, Dq), 97), _rand((B, H, Skv, Dq), 98), _rand((B, H, Skv, Dv), 99)
+    dout = _rand((B, H, Sq, Dv), 100)
+    kw = dict(scale=0.6, causal=True, bottom_right=True, window_left=2)
+    g = O.bwd(q, k, v, dout, **kw)
+    eps = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _loss(q, k, v, dout, None, **kw)
+            x[i] = old - eps
+            lm = _loss(q, k, v, dout, None, **kw)
+            x[i] = old
+            num[i] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(num - g[name])) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (name, err)
+
+
 @pytest.mark.parametrize("p", [0.0, 0.3])
 def test_backward_invariants(p):
     B, H, S, D = 1, 3, 29, 8
@@ -370,7 +455,11 @@ MUTANTS = {
     # a dropped bias term
     "bias": ("+ (h->bias ? h->bias[i * h->ld_bias + j] : 0.0)", ""),
     # an off-by-one causal boundary
-    "causal": ("if (h->causal && i < last) last = i;", "if (h->causal && i < last) last = i - 1;"),
+    "causal": ("        l = i;\n", "        l = i - 1;\n"),
+    # an off-by-one left window edge
+    "window": ("int64_t lo = i + h->band_off + h->band_lo,", "int64_t lo = i + h->band_off + h->band_lo + 1,"),
+    # the bottom-right diagonal shifted
+    "bottom_right": ("hi = i + h->band_off + h->band_hi;", "hi = i + h->band_off + h->band_hi + 1;"),
     # a wrong sign in dS
     "dS": ("double dS = s[j] * (z[j] * dot - D);", "double dS = s[j] * (z[j] * dot + D);"),
     # a transposed operand in dK
