@@ -93,7 +93,24 @@ typedef struct {
      * kv_group_size = h / h_kv).  dK and dV of a key/value head are the sums
      * over its group of query heads, accumulated in a fixed order. */
     int64_t h_kv;
+    /* Mask generality (0 keeps the plain behaviour).  Key j is visible from
+     * query i iff lo <= j - i - off <= hi, where
+     *   off = s_kv - s_q (per sequence in group mode) with
+     *         SDPA_MASK_BOTTOM_RIGHT, else 0 (top-left alignment);
+     *   lo  = -window_left with SDPA_MASK_WINDOW and window_left >= 0, else
+     *         unbounded;
+     *   hi  = window_right with SDPA_MASK_WINDOW and window_right >= 0, else
+     *         unbounded; and at most 0 when is_causal.
+     * (CK builds its mask from window_size_left / window_size_right and a
+     * top-left flag; oneDNN names top-left and bottom-right causal kinds.)
+     * A query row with no visible key gets O = 0, LSE = -inf and no
+     * gradient. */
+    uint32_t mask_flags;
+    int64_t window_left, window_right;
 } sdpa_problem_t;
+
+#define SDPA_MASK_BOTTOM_RIGHT 1u
+#define SDPA_MASK_WINDOW 2u
 
 /* Dropout keep mask (the library's own specification; the pages give the
  * ingredients - an 8-bit threshold and a 1/(1-p) rescale in CK's

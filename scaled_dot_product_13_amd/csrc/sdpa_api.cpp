@@ -11,6 +11,7 @@
 //     codes and VCHECK_SDPA_COND messages), never as exceptions.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -66,6 +67,8 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
   if (p->h_kv < 0 || (p->h_kv > 0 && p->h % p->h_kv != 0))
     return fail(SDPA_ERR_INVALID_ARG, "h_kv=%lld must be 0 or divide h=%lld", (long long)p->h_kv,
                 (long long)p->h);
+  if (p->mask_flags & ~(SDPA_MASK_BOTTOM_RIGHT | SDPA_MASK_WINDOW))
+    return fail(SDPA_ERR_INVALID_ARG, "unknown mask_flags bits 0x%x", p->mask_flags);
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
   if (p->dtype == SDPA_F32) {
@@ -84,6 +87,24 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
 
 // query heads per key/value head
 int32_t kv_group(const sdpa_problem_t* p) { return p->h_kv > 0 ? (int32_t)(p->h / p->h_kv) : 1; }
+
+// Band of the mask (see sdpa_problem_t): returns whether any key is masked
+// by it; lo, hi are clamped to +-kBandInf (sequence lengths are <= 2^30).
+bool band_of(const sdpa_problem_t* p, int32_t& br, int32_t& lo, int32_t& hi) {
+  const int64_t inf = sdpa::kBandInf;
+  const bool win = (p->mask_flags & SDPA_MASK_WINDOW) != 0;
+  int64_t l = (win && p->window_left >= 0) ? -std::min(p->window_left, inf) : -inf;
+  int64_t h = (win && p->window_right >= 0) ? std::min(p->window_right, inf) : inf;
+  if (p->is_causal) h = std::min<int64_t>(h, 0);
+  br = (p->mask_flags & SDPA_MASK_BOTTOM_RIGHT) ? 1 : 0;
+  lo = (int32_t)l;
+  hi = (int32_t)h;
+  return l > -inf || h < inf;
+}
+bool banded(const sdpa_problem_t* p) {
+  int32_t br, lo, hi;
+  return band_of(p, br, lo, hi);
+}
 
 bool empty_problem(const sdpa_problem_t* p) {
   return p->b == 0 || p->h == 0 || p->s_q == 0 || p->s_kv == 0;
@@ -214,6 +235,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.sb_ = to_str(bias_s); a.so_ = to_str(o_s);
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
   a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
+  band_of(p, a.band_br, a.band_lo, a.band_hi);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
@@ -223,7 +245,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
                  "bias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b, (long long)p->h,
                  (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk, (long long)p->d_v,
                  p->is_causal, attn_bias != nullptr, (double)p->dropout_probability, group);
-  hipError_t e = sdpa::launch_fwd(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+  hipError_t e = sdpa::launch_fwd(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a,
                                   (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -231,6 +253,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
 
 static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
   a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
+  band_of(p, a.band_br, a.band_lo, a.band_hi);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
@@ -314,7 +337,7 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   const sdpa::IoType t = io(p->dtype);
-  const bool causal = p->is_causal != 0;
+  const bool causal = banded(p);
   if (log_on())
     std::fprintf(stderr, "[sdpa] bwd dtype=%d b=%lld h=%lld s_q=%lld s_kv=%lld d=%lld/%lld causal=%d "
                  "bias=%d dbias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b,
@@ -384,7 +407,7 @@ sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.sdo_ = to_str(do_s); a.sdk_ = to_str(dk_s); a.sdv_ = to_str(dv_s); a.sdb_ = to_str(dbias_s);
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
-  hipError_t e = sdpa::launch_bwd_dkdv(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0,
+  hipError_t e = sdpa::launch_bwd_dkdv(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p),
                                        a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dK/dV launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -410,7 +433,7 @@ sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t* p, const void* q, sdpa_strides_t
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s);
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
-  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
@@ -444,7 +467,7 @@ sdpa_status_t sdpa_bwd_dq_preprocess(const sdpa_problem_t* p, const void* q, sdp
   a.sq_ = to_str(q_s); a.sk_ = to_str(k_s); a.sv_ = to_str(v_s); a.sb_ = to_str(bias_s);
   a.so_ = to_str(o_s); a.sdo_ = to_str(do_s); a.sdq_ = to_str(dq_s);
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
-  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, p->is_causal != 0, a,
+  hipError_t e = sdpa::launch_bwd_dq(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a,
                                      (hipStream_t)stream, true);
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "dQ launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;

@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
 // The two waves of a key block share a SIMD, so one's exponentials and
 // element-wise work overlap the other's matrix products, and each role keeps
 // only half of the stationary state (K and dV, or V and dK) in registers.
-template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   constexpr int BC = 128, BQ = 32, NSET = 3;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
@@ -119,8 +119,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   const int b = wi.b, hk = wi.h;
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
-  const int kv0 = wi.tile * BC;  // causal: key tile 0 has the most query tiles
+  const int kv0 = wi.tile * BC;  // top-left causal: key tile 0 has the most query tiles
   if (kv0 >= skv) return;
+  const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
 
   const T* kg = base_ptr<T>(a.k, a.sk_, sp, hk, false);
   const T* vg = base_ptr<T>(a.v, a.sv_, sp, hk, false);
@@ -141,9 +142,17 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   const float rescale = DROP ? a.drop.rescale : 1.f;
   const float c = a.scale_log2;
 
-  // causal: query rows below kv0 see none of these keys
-  const int q_begin = CAUSAL ? (kv0 / BQ) * BQ : 0;
-  const int nq = sq > q_begin ? (sq - q_begin + BQ - 1) / BQ : 0;
+  // banded: only rows [kv0 - hi, kv_last - lo] see any of these keys; the
+  // query tiles run over them from a tile boundary
+  int q_begin = 0, q_end = sq;
+  if (BAND) {
+    const int64_t kv_last = min(kv0 + BC, skv) - 1;
+    const int64_t r_lo = max((int64_t)0, (int64_t)kv0 - bd.hi);
+    const int64_t r_hi = min((int64_t)sq, kv_last - bd.lo + 1);
+    q_begin = r_lo < r_hi ? (int)(r_lo / BQ) * BQ : 0;
+    q_end = r_lo < r_hi ? (int)r_hi : 0;
+  }
+  const int nq = q_end > q_begin ? (q_end - q_begin + BQ - 1) / BQ : 0;
   // work items: item i is query tile i % nq of query head hk*G + i / nq,
   // i < G * nq; the trip loop steps them incrementally (no divisions)
   const int n_items = G * nq;
@@ -158,11 +167,14 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     }
     return it;
   };
-  if (CAUSAL && want_dbias && !roleA && kv_ok) {
-    // dBias is zero wherever the mask hides the key: rows [0, q_begin)
+  if (BAND && want_dbias && !roleA && kv_ok) {
+    // dBias is zero wherever the mask hides the key: the rows outside the
+    // query tiles
+    const int z_end = min(q_begin, sq), z_begin = min(q_begin + nq * BQ, sq);
     for (int j = 0; j < G; ++j) {
       uint16_t* dbg = dbias_head(hk * G + j);
-      for (int i = g; i < min(q_begin, sq); i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+      for (int i = g; i < z_end; i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
+      for (int i = z_begin + g; i < sq; i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
     }
   }
 
@@ -204,11 +216,14 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
+  // key - row over this wave's 32 keys and the tile's rows spans
+  // [wk0 - (q0 + BQ - 1), wk0 + 31 - q0]
   auto tile_active = [&](Item it) __attribute__((always_inline)) {
-    return wk0 < skv && (!CAUSAL || it.q0 + BQ - 1 >= wk0);
+    return wk0 < skv && (!BAND || (wk0 + 31 - it.q0 >= bd.lo && wk0 - (it.q0 + BQ - 1) <= bd.hi));
   };
   auto tile_needs_mask = [&](Item it) __attribute__((always_inline)) {
-    return (it.q0 + BQ > sq) || (wk0 + 31 >= skv) || (CAUSAL && it.q0 < wk0 + 31);
+    return (it.q0 + BQ > sq) || (wk0 + 31 >= skv) ||
+           (BAND && !(wk0 - (it.q0 + BQ - 1) >= bd.lo && wk0 + 31 - it.q0 <= bd.hi));
   };
 
   RowReader<DQK, T> rdQ;
@@ -292,7 +307,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = q0 + 16 * (r >> 3) + 8 * g + (r & 7);
-        const bool vis = qr < sq && kv_ok && (!CAUSAL || kvr <= qr);
+        const bool vis = qr < sq && kv_ok && (!BAND || (kvr - qr >= bd.lo && kvr - qr <= bd.hi));
         pv[r] = vis ? pv[r] : 0.f;
       }
     }
@@ -438,7 +453,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       } else if (i >= 1) {
         if (tile_active(prev)) {
           stepB(i - 1, set_prev, prev, reg, acc);
-        } else if (CAUSAL && want_dbias && kv_ok) {
+        } else if (BAND && want_dbias && kv_ok) {
           // the whole tile is hidden from my key
           uint16_t* dbg = dbias_head(prev.h);
           for (int r = prev.q0 + g; r < min(prev.q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
@@ -488,7 +503,7 @@ template <int DQK, int DV, bool DROP> struct DqOcc {
 // With PRE the kernel also does the preprocess for its rows: D from the O
 // and dO rows it loads and LSE*log2(e) from the forward's LSE, both written
 // to the stats for the dK/dV kernel, which then runs after it.
-template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP, bool PRE>
+template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP, bool PRE>
 __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(const BwdArgs a) {
   constexpr int BR = 128, BC = 64;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32;
@@ -501,7 +516,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_DQ_HEAD_GROUP);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
-  const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
+  const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest top-left causal tiles first
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
   const int q0 = mt * BR;
@@ -514,9 +529,15 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
 
-  const int kv_end = CAUSAL ? min(skv, q0 + BR) : skv;
-  const int nt = (kv_end + BC - 1) / BC;
+  // banded: the tile's rows see only keys [q0 + lo, r_last + hi]
+  const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
+  const int r_last = min(q0 + BR, sq) - 1;
+  const int k_begin = BAND ? max(0, q0 + bd.lo) : 0;
+  const int k_end = BAND ? (int)min((int64_t)r_last + bd.hi + 1, (int64_t)skv) : skv;
+  const int t0 = k_begin / BC;
+  const int nt = k_end > k_begin ? (k_end + BC - 1) / BC - t0 : 0;
   const int row = q0 + 32 * w + l32;
+  const int wq0 = q0 + 32 * w;  // this wave's first row
   const bool row_ok = row < sq;
 
   u32x4 qreg[KT], doreg[VT];
@@ -571,8 +592,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   ldK.init(kg, a.sk_.s, w, lane);
   ldV.init(vg, a.sv_.s, w, lane);
   if (nt > 0) {
-    ldK.load(sK[0], 0, skv, w, lane);
-    ldV.load(sV[0], 0, skv, w, lane);
+    ldK.load(sK[0], t0 * BC, skv, w, lane);
+    ldV.load(sV[0], t0 * BC, skv, w, lane);
   }
   RowReader<DQK, T> rdK;
   RowReader<DV, T> rdV;
@@ -586,10 +607,12 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   // `nK`, `nV`; alternate tiles swap the buffers so that LDS addresses are
   // compile-time offsets from per-lane bases.
   auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV) __attribute__((always_inline)) {
-    const int n0 = it * BC;
+    const int n0 = (t0 + it) * BC;
     wait_all();
     __syncthreads();
-    const bool active = !CAUSAL || (n0 <= q0 + 32 * w + 31);
+    // key - row over the tile's keys and this wave's rows spans
+    // [n0 - (wq0 + 31), n0 + BC - 1 - wq0]
+    const bool active = !BAND || (n0 - (wq0 + 31) <= bd.hi && n0 + BC - 1 - wq0 >= bd.lo);
 
     uint32_t braw[4][4];
     if (BIAS && active) {
@@ -639,7 +662,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
 
     // P^T = exp2(scale log2e S^T (+ log2e bias) - LSE log2e).  Rows past s_q
     // have Q = dO = 0 and LSE = D = 0, so their dS is exactly 0 without a
-    // mask; keys past s_kv or above the diagonal are zeroed on the tiles
+    // mask; keys past s_kv or outside the band are zeroed on the tiles
     // that have them.
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -655,7 +678,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
         }
         s[blk][r] = __builtin_amdgcn_exp2f(x);
       }
-    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > q0 + 32 * w);
+    const bool need_mask =
+        (n0 + BC > skv) || (BAND && !(n0 - (wq0 + 31) >= bd.lo && n0 + BC - 1 - wq0 <= bd.hi));
     if (need_mask) {
       keep_branch();
 #pragma unroll
@@ -663,7 +687,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-          const bool vis = kv < skv && (!CAUSAL || kv <= row);
+          const bool vis = kv < skv && (!BAND || (kv - row >= bd.lo && kv - row <= bd.hi));
           s[blk][r] = vis ? s[blk][r] : 0.f;
         }
     }
@@ -717,7 +741,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
 
 // ---------------------------------------------------------------------------
 // fp32 io: one wavefront per query row (dQ) or per key (dK, dV, dBias).
-template <bool CAUSAL, bool BIAS, bool DROP>
+template <bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.z, h = blockIdx.y;
@@ -745,9 +769,13 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
     dO[c] = d < dv ? doi[d] : 0.f;
     acc[c] = 0.f;
   }
-  int last = sp.skv - 1;
-  if (CAUSAL && i < last) last = i;
-  for (int j = 0; j <= last; ++j) {
+  int first = 0, last = sp.skv - 1;
+  if (BAND) {
+    const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sp.sq, sp.skv);
+    first = (int)max((int64_t)0, (int64_t)i + bd.lo);
+    last = (int)min((int64_t)last, (int64_t)i + bd.hi);
+  }
+  for (int j = first; j <= last; ++j) {
     const float* kj = kg + (int64_t)j * a.sk_.s;
     const float* vj = vg + (int64_t)j * a.sv_.s;
     float ps = 0.f, pd = 0.f;
@@ -777,7 +805,7 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
   }
 }
 
-template <bool CAUSAL, bool BIAS, bool DROP>
+template <bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.z, hk = blockIdx.y;  // key/value head
@@ -797,7 +825,13 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
     gk[c] = 0.f;
     gv[c] = 0.f;
   }
-  const int i0 = CAUSAL ? min(j, sp.sq) : 0;
+  // rows that see key j: [j - hi, j - lo] within the sequence
+  int i0 = 0, i1 = sp.sq;
+  if (BAND) {
+    const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sp.sq, sp.skv);
+    i0 = (int)min((int64_t)sp.sq, max((int64_t)0, (int64_t)j - bd.hi));
+    i1 = (int)max((int64_t)i0, min((int64_t)sp.sq, (int64_t)j - bd.lo + 1));
+  }
   // the query heads of this key/value head's group, in ascending order
   for (int h = hk * a.G; h < (hk + 1) * a.G; ++h) {
     const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true);
@@ -809,9 +843,11 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
                        : nullptr;
     const uint32_t bh = (uint32_t)(b * a.H + h);
     const int64_t d_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
-    if (dbcol && lane == 0)
+    if (dbcol && lane == 0) {
       for (int i = 0; i < i0; ++i) dbcol[(int64_t)i * a.sdb_.s] = 0.f;
-    for (int i = i0; i < sp.sq; ++i) {
+      for (int i = i1; i < sp.sq; ++i) dbcol[(int64_t)i * a.sdb_.s] = 0.f;
+    }
+    for (int i = i0; i < i1; ++i) {
       const float* qi = qg + (int64_t)i * a.sq_.s;
       const float* doi = dog + (int64_t)i * a.sdo_.s;
       float ps = 0.f, pd = 0.f;

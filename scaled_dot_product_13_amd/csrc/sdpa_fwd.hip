@@ -34,7 +34,7 @@ template <int DQK, int DV, bool DROP> struct FwdOcc {
   static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
 };
 
-template <typename T, int DQK, int DV, bool CAUSAL, bool BIAS, bool DROP>
+template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(const FwdArgs a) {
   constexpr int BR = 128;
   constexpr int NBLK = SDPA_FWD_NBLK;  // 32-key blocks per key tile
@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
-  const int mt = CAUSAL ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
+  const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
   const SeqPos sp = resolve_seq(a.seq, b);
   const int sq = sp.sq, skv = sp.skv;
   const int q0 = mt * BR;
@@ -65,8 +65,14 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
 
-  const int kv_end = CAUSAL ? min(skv, q0 + BR) : skv;
-  const int nt = (kv_end + BC - 1) / BC;
+  // keys visible from some row of this tile: [k_begin, k_end), in key
+  // tiles t0 .. t0 + nt - 1
+  const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
+  const int r_last = min(q0 + BR, sq) - 1;
+  const int k_begin = BAND ? max(0, q0 + bd.lo) : 0;
+  const int k_end = BAND ? min(skv, (int)min((int64_t)r_last + bd.hi + 1, (int64_t)skv)) : skv;
+  const int t0 = k_begin / BC;
+  const int nt = k_end > k_begin ? (k_end + BC - 1) / BC - t0 : 0;
   const int wq0 = q0 + 32 * w;        // this wave's first query row
   const int row = wq0 + l32;          // this lane's query row
   const bool row_ok = row < sq;
@@ -76,8 +82,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   ldK.init(base_ptr<T>(a.k, a.sk_, sp, h / a.G, false), a.sk_.s, w, lane);
   ldV.init(base_ptr<T>(a.v, a.sv_, sp, h / a.G, false), a.sv_.s, w, lane);
   if (nt > 0) {
-    ldK.load(sK[0], 0, skv, w, lane);
-    ldV.load(sV[0], 0, skv, w, lane);
+    ldK.load(sK[0], t0 * BC, skv, w, lane);
+    ldV.load(sV[0], t0 * BC, skv, w, lane);
   }
 
   u32x4 qreg[KT];
@@ -111,12 +117,13 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   // `nK`, `nV`.  Called with the two buffers swapped on alternate tiles so
   // that every LDS address is a compile-time offset from a per-lane base.
   auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV) __attribute__((always_inline)) {
-    const int n0 = it * BC;
+    const int n0 = (t0 + it) * BC;
     wait_all();       // this wave's part of tile `it` has landed
     __syncthreads();  // ... and everyone's; tile it-1 is fully consumed
 
-    // a wave whose rows see none of this tile skips it (causal)
-    const bool active = !CAUSAL || n0 <= wq0 + 31;
+    // a wave whose rows see none of this tile skips it (band mask): its rows
+    // [wq0, wq0 + 31] see keys [wq0 + lo, wq0 + 31 + hi]
+    const bool active = !BAND || (n0 <= wq0 + 31 + bd.hi && n0 + BC - 1 >= wq0 + bd.lo);
 
     // All K operands of this tile are requested first, so their LDS latency
     // overlaps the prefetch issue and the rest of the requests.
@@ -175,10 +182,12 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 
     // Scores in scaled log2 units.  Without bias the scale is folded into
     // the exponent's FMA and the row max is taken on the raw scores.
-    const bool need_mask = (n0 + BC > skv) || (CAUSAL && n0 + BC - 1 > wq0);
+    // masked unless every (row, key) of the wave's tile lies inside the band
+    const bool need_mask =
+        (n0 + BC > skv) || (BAND && !(n0 - (wq0 + 31) >= bd.lo && n0 + BC - 1 - wq0 <= bd.hi));
     auto visible = [&](int blk, int r) {
       int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-      return kv < skv && (!CAUSAL || kv <= row);
+      return kv < skv && (!BAND || (kv - row >= bd.lo && kv - row <= bd.hi));
     };
     float mrow;
     if (BIAS) {
@@ -285,7 +294,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           int kv = kv0 + e;
-          if (kv < skv && (!CAUSAL || kv <= row))
+          if (kv < skv && (!BAND || (kv - row >= bd.lo && kv - row <= bd.hi)))
             kp[kv] = ((kw[k] >> (8 * e)) & 0xffu) >= dk.thr ? 1 : 0;
         }
       }
@@ -323,7 +332,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
 }
 
 // fp32 io: one wavefront per query row, the head dims spread over lanes.
-template <bool CAUSAL, bool BIAS, bool DROP>
+template <bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.z, h = blockIdx.y;
@@ -347,10 +356,14 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
     q[c] = d < dqk ? qg[d] : 0.f;
     o[c] = 0.f;
   }
-  int last = sp.skv - 1;
-  if (CAUSAL && row < last) last = row;
+  int first = 0, last = sp.skv - 1;
+  if (BAND) {
+    const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sp.sq, sp.skv);
+    first = (int)max((int64_t)0, (int64_t)row + bd.lo);
+    last = (int)min((int64_t)last, (int64_t)row + bd.hi);
+  }
   float m = -INFINITY, l = 0.f;
-  for (int j = 0; j <= last; ++j) {
+  for (int j = first; j <= last; ++j) {
     const float* kj = kg + (int64_t)j * a.sk_.s;
     float part = 0.f;
 #pragma unroll

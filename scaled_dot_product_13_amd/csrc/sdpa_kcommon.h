@@ -86,6 +86,21 @@ inline dim3 xcd_grid(int ntiles, int H, int B) {
   return dim3((unsigned)(8 * ((BH + 7) / 8) * ntiles), 1, 1);
 }
 
+// The band of a sequence: key j is visible from row i iff
+// lo <= j - i <= hi (the mask's lo/hi shifted by the bottom-right offset
+// s_kv - s_q when br is set), clamped to +-kBandInf.
+struct Band {
+  int32_t lo, hi;
+};
+__device__ __forceinline__ Band seq_band(int32_t br, int32_t lo, int32_t hi, int sq, int skv) {
+  const int64_t off = br ? (int64_t)skv - sq : 0;
+  const int64_t l = off + lo, h = off + hi;
+  Band b;
+  b.lo = (int32_t)(l < -kBandInf ? -kBandInf : (l > kBandInf ? kBandInf : l));
+  b.hi = (int32_t)(h < -kBandInf ? -kBandInf : (h > kBandInf ? kBandInf : h));
+  return b;
+}
+
 struct DropKey {
   uint32_t k0, k1, off, thr;
 };

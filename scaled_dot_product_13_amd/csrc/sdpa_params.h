@@ -31,6 +31,8 @@ struct DropoutArgs {
   const uint64_t* seed_offset_dev;  // optional device {seed, offset}
 };
 
+constexpr int32_t kBandInf = 1 << 30;
+
 struct FwdArgs {
   const void *q, *k, *v, *bias;
   void* o;
@@ -40,6 +42,9 @@ struct FwdArgs {
   int32_t bias_vec;  // bias rows 16-byte aligned: vector loads allowed
   int32_t B, H;
   int32_t G;           // query heads per key/value head (K/V head of h is h / G)
+  // band mask: key j visible from row i iff lo <= j - i - off <= hi, with
+  // off = s_kv - s_q (per sequence) when band_br, else 0; +-kBandInf = unbounded
+  int32_t band_br, band_lo, band_hi;
   SeqInfo seq;
   float scale;         // scaling_factor
   float scale_log2;    // scaling_factor * log2(e)
@@ -58,6 +63,9 @@ struct BwdArgs {
   int32_t bias_vec;
   int32_t B, H;
   int32_t G;  // query heads per key/value head (K/V head of h is h / G)
+  // band mask: key j visible from row i iff lo <= j - i - off <= hi, with
+  // off = s_kv - s_q (per sequence) when band_br, else 0; +-kBandInf = unbounded
+  int32_t band_br, band_lo, band_hi;
   SeqInfo seq;
   float scale, scale_log2;
   DropoutArgs drop;

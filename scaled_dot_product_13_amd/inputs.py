@@ -8,7 +8,8 @@ Recipe: a torch CPU generator seeded with `seed` draws, in order,
 (group mode only) the sequence lengths with randint(lo, hi+1), then
 Q, K, V, [bias], dO as float32 standard normals, each then rounded to the io
 dtype (round to nearest even).  Tensors are dense BHSD (batch mode) or packed
-THD with cu_seqlens = [0, cumsum(lengths)] (group mode).
+THD with cu_seqlens = [0, cumsum(lengths)] (group mode); K and V use the
+same lengths unless explicit key/value lengths are given.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -38,6 +39,12 @@ class Workload:
     varlen: Optional[tuple] = None  # (n_seq, lo, hi)
     scale: Optional[float] = None
     h_kv: Optional[int] = None  # key/value heads (grouped-query); None = h
+    # mask band beyond top-left causal: key j is visible from row i iff
+    # -window_left <= j - i - off <= window_right (None = unbounded side,
+    # causal caps the right side at 0), off = s_kv - s_q with bottom_right
+    bottom_right: bool = False
+    window_left: Optional[int] = None
+    window_right: Optional[int] = None
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,9 +66,10 @@ WORKLOADS = {
 }
 
 
-def make_inputs(wl: Workload, lengths=None):
+def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
     """Draw the workload's tensors on the CPU.  Returns a dict with
-    q, k, v, dout, [bias], [lengths, cu_seqlens] and the io dtype."""
+    q, k, v, dout, [bias], [lengths, cu_seqlens, max_seqlen and their _kv
+    twins] and the io dtype."""
     g = torch.Generator().manual_seed(wl.seed)
     io = _IO[wl.dtype]
     out = {"dtype": io}
@@ -71,14 +79,23 @@ def make_inputs(wl: Workload, lengths=None):
             lengths = torch.randint(lo, hi + 1, (n,), generator=g)
         else:
             lengths = torch.as_tensor(lengths, dtype=torch.int64)
-        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
-        cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
-        T = int(cu[-1])
+        kv_lengths = lengths if kv_lengths is None else torch.as_tensor(kv_lengths, dtype=torch.int64)
+        assert len(kv_lengths) == len(lengths)
+
+        def cumulative(ls):
+            cu = torch.zeros(len(ls) + 1, dtype=torch.int32)
+            cu[1:] = torch.cumsum(ls, 0).to(torch.int32)
+            return cu
+        cu, cu_kv = cumulative(lengths), cumulative(kv_lengths)
+        T, Tk = int(cu[-1]), int(cu_kv[-1])
         hk = wl.h_kv or wl.h
-        shp_q, shp_k, shp_v, shp_o = (T, wl.h, wl.d_qk), (T, hk, wl.d_qk), (T, hk, wl.d_v), (T, wl.h, wl.d_v)
+        shp_q, shp_k, shp_v, shp_o = (T, wl.h, wl.d_qk), (Tk, hk, wl.d_qk), (Tk, hk, wl.d_v), (T, wl.h, wl.d_v)
         out["lengths"] = lengths
         out["cu_seqlens"] = cu
         out["max_seqlen"] = int(lengths.max()) if len(lengths) else 0
+        out["kv_lengths"] = kv_lengths
+        out["cu_seqlens_kv"] = cu_kv
+        out["max_seqlen_kv"] = int(kv_lengths.max()) if len(kv_lengths) else 0
     else:
         hk = wl.h_kv or wl.h
         shp_q = (wl.b, wl.h, wl.s_q, wl.d_qk)
@@ -96,7 +113,10 @@ def make_inputs(wl: Workload, lengths=None):
 
 
 def small(dtype="bf16", b=1, h=2, s_q=200, s_kv=200, d_qk=128, d_v=128, causal=False,
-          bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None, h_kv=None) -> Workload:
+          bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None, h_kv=None,
+          bottom_right=False, window_left=None, window_right=None) -> Workload:
     """A small workload (parity-test size) with the same recipe."""
     return Workload(f"small-{dtype}", dtype, b, h, s_q, s_kv, d_qk, d_v, causal=causal, bias=bias,
-                    dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale, h_kv=h_kv)
+                    dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale, h_kv=h_kv,
+                    bottom_right=bottom_right, window_left=window_left,
+                    window_right=window_right)

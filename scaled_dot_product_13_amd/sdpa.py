@@ -45,7 +45,13 @@ class Problem(ctypes.Structure):
         ("dropout_seed_offset_dev", ctypes.c_void_p),
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
         ("h_kv", ctypes.c_int64),
+        ("mask_flags", ctypes.c_uint32), ("window_left", ctypes.c_int64),
+        ("window_right", ctypes.c_int64),
     ]
+
+
+MASK_BOTTOM_RIGHT = 1
+MASK_WINDOW = 2
 
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -128,9 +134,13 @@ def _stream():
 
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
-                 max_seqlen_kv=None):
+                 max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None):
     """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group
-    [T,H,D]); k and v may have fewer heads than q (grouped-query attention)."""
+    [T,H,D]); k and v may have fewer heads than q (grouped-query attention).
+
+    Mask: row i sees key j iff -window_left <= j - i - off <= window_right
+    (a window side that is None is unbounded; causal caps window_right at 0),
+    off = s_kv - s_q per sequence with bottom_right, else 0."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     group = cu_seqlens_q is not None
@@ -151,6 +161,10 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     p.h_kv = k.shape[1]
     p.scaling_factor = float(scale if scale is not None else 1.0 / math.sqrt(p.d_qk))
     p.is_causal = 1 if causal else 0
+    windowed = window_left is not None or window_right is not None
+    p.mask_flags = (MASK_BOTTOM_RIGHT if bottom_right else 0) | (MASK_WINDOW if windowed else 0)
+    p.window_left = -1 if window_left is None else int(window_left)
+    p.window_right = -1 if window_right is None else int(window_right)
     p.dropout_probability = float(dropout_p)
     p.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     p.dropout_offset = int(offset) & 0xFFFFFFFFFFFFFFFF
@@ -160,13 +174,15 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
 
 def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
              seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
-             max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None):
+             max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None,
+             bottom_right=False, window_left=None, window_right=None):
     """Forward.  Returns (o, lse or None, keep or None)."""
     group = cu_seqlens_q is not None
     p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
                      offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
-                     max_seqlen_kv=max_seqlen_kv)
+                     max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
+                     window_left=window_left, window_right=window_right)
     if out is None:
         oshape = list(q.shape)
         oshape[-1] = v.shape[-1]
@@ -188,13 +204,15 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
 
 def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, dropout_p=0.0,
              seed=0, offset=0, seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None,
-             max_seqlen_q=None, max_seqlen_kv=None, want_dbias=False, workspace=None):
+             max_seqlen_q=None, max_seqlen_kv=None, want_dbias=False, workspace=None,
+             bottom_right=False, window_left=None, window_right=None):
     """Backward.  Returns (dq, dk, dv, dbias or None)."""
     group = cu_seqlens_q is not None
     p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
                      offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
-                     max_seqlen_kv=max_seqlen_kv)
+                     max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
+                     window_left=window_left, window_right=window_right)
     if dout.stride(-1) != 1:
         dout = dout.contiguous()
     dq, dk, dv = _alloc_like(q, q.shape), _alloc_like(k, k.shape), _alloc_like(v, v.shape)

@@ -54,6 +54,8 @@ def _problem(S, **kw):
     if "cu_kv" in kw:
         p.cu_seqlens_kv = kw["cu_kv"]
     p.h_kv = kw.get("hkv", 0)
+    p.mask_flags = kw.get("mask_flags", 0)
+    p.window_left, p.window_right = kw.get("window", (-1, -1))
     return p
 
 
@@ -101,6 +103,19 @@ def test_invalid_arguments(S):
     assert b"h_kv" in L.sdpa_last_error_message()
     assert _fwd(S, _problem(S, h=4, hkv=-1)) == S.SDPA_ERR_INVALID_ARG
     assert _bwd(S, _problem(S, h=6, hkv=4)) == S.SDPA_ERR_INVALID_ARG
+    # only the bottom-right and window bits are defined
+    assert _fwd(S, _problem(S, mask_flags=4)) == S.SDPA_ERR_INVALID_ARG
+    assert b"mask_flags" in L.sdpa_last_error_message()
+    assert _bwd(S, _problem(S, mask_flags=0x80000000)) == S.SDPA_ERR_INVALID_ARG
+
+
+def test_problem_struct_matches_the_header(S):
+    # the binding's struct mirrors sdpa_problem_t field by field
+    hdr = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    end = hdr.index("} sdpa_problem_t;")
+    body = hdr[hdr.rindex("typedef struct", 0, end):end]
+    fields = re.findall(r"\b([a-z_0-9]+)\s*[;,]", body)
+    assert [n for n, _ in S.Problem._fields_] == fields
 
 
 def test_unsupported_combinations(S):

@@ -17,8 +17,8 @@ Tolerances (written here, used everywhere below):
                    type (values reach ~10), and P_ij (<= 1) times the error
                    of D_i = rowsum(dO o O), which the backward takes from the
                    forward's io-typed O while the oracle uses its fp64 O.
-  LSE (all io)   : max|gpu - ref| <= 1e-3
-  keep mask      : bit-exact on every position the causal mask leaves visible
+  LSE (all io)   : max|gpu - ref| <= 1e-3; rows that see no key: -inf on both
+  keep mask      : bit-exact on every position the mask leaves visible
 """
 import sys
 
@@ -58,6 +58,11 @@ def _cmp(name, got, ref, dtype, dD=None):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if name == "lse":
+        # rows that see no key under the mask have LSE = -inf
+        empty = np.isneginf(ref)
+        assert np.array_equal(np.isneginf(got), empty), "LSE -inf rows differ"
+        got, ref = got[~empty], ref[~empty]
     assert np.all(np.isfinite(ref)), name
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     if name == "lse":
@@ -74,10 +79,28 @@ def _cmp(name, got, ref, dtype, dD=None):
     return err
 
 
-def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"):
+def _visible(sq, skv, wl):
+    """Positions the workload's mask leaves visible (for the keep mask)."""
+    i = np.arange(sq)[:, None]
+    j = np.arange(skv)[None, :]
+    d = j - i - ((skv - sq) if wl.bottom_right else 0)
+    lo = -wl.window_left if wl.window_left is not None else -np.inf
+    hi = wl.window_right if wl.window_right is not None else np.inf
+    if wl.causal:
+        hi = min(hi, 0)
+    return (d >= lo) & (d <= hi)
+
+
+def _mask_kw(wl):
+    return dict(bottom_right=wl.bottom_right, window_left=wl.window_left,
+                window_right=wl.window_right)
+
+
+def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd",
+                 kv_lengths=None):
     """Run fwd+bwd on the GPU and compare with the oracle on `heads`
     (all heads when None).  Returns the max errors."""
-    x = inputs.make_inputs(wl, lengths)
+    x = inputs.make_inputs(wl, lengths, kv_lengths)
     dev = "cuda"
     group = wl.varlen is not None
     q, k, v, dout = (x[n] for n in ("q", "k", "v", "dout"))
@@ -88,23 +111,23 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
         gq, gk, gv, gdo = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (gq, gk, gv, gdo))
     gb = bias.to(dev) if bias is not None else None
     kw = dict(scale=wl.softmax_scale, causal=wl.causal, dropout_p=wl.dropout_p,
-              seed=inputs.DROPOUT_SEED, offset=0)
+              seed=inputs.DROPOUT_SEED, offset=0, **_mask_kw(wl))
     if group:
-        cu = x["cu_seqlens"].to(dev)
-        kw.update(cu_seqlens_q=cu, cu_seqlens_kv=cu, max_seqlen_q=x["max_seqlen"],
-                  max_seqlen_kv=x["max_seqlen"])
+        kw.update(cu_seqlens_q=x["cu_seqlens"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
+                  max_seqlen_q=x["max_seqlen"], max_seqlen_kv=x["max_seqlen_kv"])
     want_keep = check_keep and wl.dropout_p > 0 and not group
     _say(wl.name, wl.dtype, "B", wl.b, "H", wl.h, "Sq", wl.s_q, "Skv", wl.s_kv, "d", wl.d_qk,
-         wl.d_v, "causal", wl.causal, "bias", wl.bias, "p", wl.dropout_p, "group", group, layout)
+         wl.d_v, "causal", wl.causal, "bias", wl.bias, "p", wl.dropout_p, "group", group, layout,
+         "mask", _mask_kw(wl))
     o, lse, keep = S.sdpa_fwd(gq, gk, gv, bias=gb, return_keep=want_keep, **kw)
     dq, dk, dv, dbias = S.sdpa_bwd(gq, gk, gv, o, gdo, lse, bias=gb, want_dbias=bias is not None, **kw)
     torch.cuda.synchronize()
 
     okw = dict(scale=wl.softmax_scale, causal=wl.causal, p_drop=wl.dropout_p,
-               seed=inputs.DROPOUT_SEED, offset=0)
+               seed=inputs.DROPOUT_SEED, offset=0, **_mask_kw(wl))
     if group:
-        cun = x["cu_seqlens"].numpy().astype(np.int64)
-        okw.update(cu_seqlens_q=cun, cu_seqlens_kv=cun)
+        okw.update(cu_seqlens_q=x["cu_seqlens"].numpy().astype(np.int64),
+                   cu_seqlens_kv=x["cu_seqlens_kv"].numpy().astype(np.int64))
     f64 = lambda t: t.double().numpy() if t is not None else None
     ref = O.bwd(f64(q), f64(k), f64(v), f64(dout), bias=f64(bias), heads=heads, **okw)
     rkeep = None
@@ -130,11 +153,13 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
     for (b, h) in heads:
         if group:
             c0, c1 = int(x["cu_seqlens"][b]), int(x["cu_seqlens"][b + 1])
-            sl = slice(c0, c1)
+            k0, k1 = int(x["cu_seqlens_kv"][b]), int(x["cu_seqlens_kv"][b + 1])
             for name, t in got.items():
                 hh = head_of(name, b, h)
+                sl = slice(k0, k1) if name in ("dk", "dv") else slice(c0, c1)
                 if hh is not None:
                     errs[name] = max(errs.get(name, 0), _cmp(name, _np(t[sl, hh]), ref[name][sl, hh], x["dtype"]))
+            sl = slice(c0, c1)
             errs["lse"] = max(errs.get("lse", 0), _cmp("lse", _np(lse[h, sl]), ref["lse"][h, sl], x["dtype"]))
         else:
             dD = np.sum(dout[b, h].double().numpy() * (_np(o[b, h]) - ref["o"][b, h]), -1)
@@ -146,11 +171,8 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
             if want_keep:
                 gk_ = keep[b, h].cpu().numpy()
                 rk = rkeep[b, h]
-                if wl.causal:
-                    vis = np.tril(np.ones(rk.shape, dtype=bool))
-                    assert np.array_equal(gk_[vis], rk[vis]), "keep mask differs"
-                else:
-                    assert np.array_equal(gk_, rk), "keep mask differs"
+                vis = _visible(wl.s_q, wl.s_kv, wl)
+                assert np.array_equal(gk_[vis], rk[vis]), "keep mask differs"
     _say("max errors", {k_: float("%.3g" % v_) for k_, v_ in errs.items()})
     return errs
 
@@ -200,6 +222,49 @@ def test_grouped_query_varlen(S):
     wl = inputs.small("bf16", b=len(lengths), h=4, h_kv=2, d_qk=128, d_v=128, causal=True, seed=91,
                       varlen=(len(lengths), 1, 257))
     run_workload(S, wl, lengths=lengths)
+
+
+# Masks beyond top-left causal: bottom-right alignment (s_q != s_kv) and
+# sliding windows, alone and with bias and dropout.
+MASKS = [
+    # dtype, dims, s_q, s_kv, causal, bias, p, bottom_right, window_left, window_right
+    ("bf16", (128, 128), 150, 400, True, False, 0.0, True, None, None),
+    ("bf16", (128, 128), 300, 140, True, False, 0.0, True, None, None),  # rows without keys
+    ("f16", (64, 64), 257, 257, True, False, 0.0, False, 100, None),
+    ("bf16", (128, 128), 300, 300, False, False, 0.0, False, 64, 32),
+    ("f16", (128, 128), 200, 330, True, True, 0.1, True, 50, None),
+    ("bf16", (192, 128), 160, 160, False, True, 0.0, False, 0, 0),
+    ("bf16", (64, 64), 130, 260, False, False, 0.0, True, 10, 20),
+    ("bf16", (128, 128), 333, 333, False, True, 0.0, False, 200, None),
+    ("bf16", (128, 128), 100, 100, True, False, 0.1, False, 1000, None),
+    ("f16", (192, 128), 260, 100, False, False, 0.0, True, 30, 40),  # rows without keys
+    ("f32", (64, 64), 90, 70, True, True, 0.1, True, 30, None),
+    ("f32", (64, 64), 100, 100, False, False, 0.0, False, 5, 200),
+]
+
+
+@pytest.mark.parametrize("case", MASKS, ids=lambda c: f"{c[0]}-d{c[1][0]}-{c[2]}x{c[3]}-c{int(c[4])}"
+                         f"-b{int(c[5])}-p{c[6]}-br{int(c[7])}-w{c[8]},{c[9]}")
+def test_mask_parity(S, case):
+    dt, (dq_, dv_), sq, skv, causal, bias, p, br, wl_, wr_ = case
+    wl = inputs.small(dt, b=2, h=2, s_q=sq, s_kv=skv, d_qk=dq_, d_v=dv_, causal=causal, bias=bias,
+                      dropout_p=p, seed=sq * 3 + skv, bottom_right=br, window_left=wl_,
+                      window_right=wr_)
+    run_workload(S, wl)
+
+
+def test_mask_varlen_bottom_right(S):
+    # per-sequence bottom-right offsets s_kv - s_q of both signs
+    lengths, kv_lengths = [100, 300, 1, 64], [250, 130, 40, 64]
+    wl = inputs.small("bf16", b=4, h=4, h_kv=2, d_qk=128, d_v=128, causal=True, seed=17,
+                      varlen=(4, 1, 300), bottom_right=True, window_left=90)
+    run_workload(S, wl, lengths=lengths, kv_lengths=kv_lengths)
+
+
+def test_mask_grouped_query_window(S):
+    wl = inputs.small("f16", b=1, h=4, h_kv=1, s_q=260, s_kv=260, d_qk=128, d_v=128, causal=False,
+                      bias=True, seed=23, window_left=40, window_right=70)
+    run_workload(S, wl)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
