@@ -10,7 +10,13 @@ Throughput uses the workload's algorithmic flop count: forward
 4*b*h*s_q*s_kv*d (2*b*h*s_q*s_kv*(d_qk+d_v) in general), backward 2.5x that,
 both halved under the causal mask.  Prints one JSON line (rank 0, N = 1).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+The line also carries a "decode" object: the thin-query forward (split-KV)
+on the decode workload (bf16, B=16, 32 query heads over 8 key/value heads,
+one query row per sequence, S_kv=8192, d=128), timed the same way and
+reported as algorithmic HBM bytes (K, V, Q, O, LSE) per second against the
+8 TB/s peak.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
 import argparse
 import hashlib
@@ -82,6 +88,44 @@ def cpu_baseline(wl, x, budget_heads):
                       f"same workload, fp64, {dt:.1f} s wall"}
 
 
+def decode_bench(S, torch, steps, warmup):
+    """Time the thin-query forward on the decode workload: HIP events on the
+    launch stream around each sdpa_fwd call (the split kernel and, when the
+    keys are split, the combine kernel)."""
+    from scaled_dot_product_13_amd import inputs
+    wl = inputs.DECODE
+    x = inputs.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    del x
+    kw = dict(scale=wl.softmax_scale, causal=wl.causal, bottom_right=wl.bottom_right)
+    o = torch.empty((wl.b, wl.h, wl.s_q, wl.d_v), dtype=q.dtype, device=dev)
+    lse = torch.empty((wl.b, wl.h, wl.s_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(S.fwd_workspace_size(q, k, v, **kw), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        S.sdpa_fwd(q, k, v, out=o, lse=lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        S.sdpa_fwd(q, k, v, out=o, lse=lse, workspace=ws, **kw)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    hk = wl.h_kv or wl.h
+    es = 2  # bf16
+    byts = (es * wl.b * hk * wl.s_kv * (wl.d_qk + wl.d_v)        # K, V
+            + es * wl.b * wl.h * wl.s_q * (wl.d_qk + wl.d_v)     # Q, O
+            + 4 * wl.b * wl.h * wl.s_q)                          # LSE
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": wl.name, "ms": round(ms, 5), "bytes": byts,
+            "roofline": {"kernel": "fwd_decode (+ combine)", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +133,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload index (2 = headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the thin-query (decode) line")
     ap.add_argument("--cpu-heads", type=int, default=1 << 30,
                     help="(batch, head) slices the CPU baseline times (default: all)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -193,6 +238,8 @@ def main():
                 "kernels_ms": {n: round(avg[n], 5) for n in ("bwd_dq", "bwd_dkdv")}},
         "roofline": roof,
     }
+    if not args.no_decode:
+        out["decode"] = decode_bench(S, torch, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
     else:

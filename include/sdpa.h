@@ -144,6 +144,15 @@ size_t sdpa_bwd_workspace_size(const sdpa_problem_t *problem);
  *   dropout_keep_out: nullable debug output, dense uint8 [b,h,s_q,s_kv]
  *     (batch mode only): 1 where the element was kept.  Positions the causal
  *     mask hides are left unwritten.
+ *   workspace: thin-query problems (16-bit io, s_q <= 16, no bias, p = 0;
+ *     decoding, as oneDNN's thin-q configuration and its single-query
+ *     batching over key/value heads) run a split-KV kernel that packs the
+ *     query heads of each key/value head into one tile and splits the keys
+ *     over workgroups.  Its partial results need
+ *     sdpa_fwd_workspace_size(problem) bytes (16-byte aligned); with less
+ *     (or null) the same kernel runs unsplit, which is correct but slower
+ *     when few (batch, key/value head) pairs exist.  Other problems take no
+ *     workspace.  Results do not depend on the split beyond rounding.
  * Errors: SDPA_ERR_INVALID_ARG for null tensors, bad strides, p outside
  * [0,1) or half the varlen pair; SDPA_ERR_UNSUPPORTED for head dims outside
  * the compiled set (16-bit io: (d_qk, d_v) in {(64,64), (128,128),

@@ -7,7 +7,7 @@ before the library exists; touching any API name without a built library
 raises ImportError (there is no fallback path).
 """
 _API = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_preprocess", "sdpa_bwd_dkdv", "sdpa_bwd_dq",
-        "sdpa_bwd_dq_preprocess", "stats_layout",
+        "sdpa_bwd_dq_preprocess", "stats_layout", "fwd_workspace_size",
         "make_problem", "SdpaError",
         "version", "Problem", "Strides")
 

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libsdpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sdpa_fwd.hip", "sdpa_bwd.hip", "sdpa_api.cpp"]
+SOURCES = ["sdpa_fwd.hip", "sdpa_decode.hip", "sdpa_bwd.hip", "sdpa_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # packed fp32 VALU ops stay disabled for all device code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -174,6 +174,39 @@ float* stats_lse2(const sdpa_problem_t* p, const float* stats) {
   return (float*)((const char*)stats + stats_half_bytes(p));
 }
 
+// Thin-query forward: 16-bit io, at most kDecodeMaxSq query rows per
+// sequence, no bias and no dropout (SDPA_DECODE=0 turns the path off).
+bool decode_eligible(const sdpa_problem_t* p, bool has_bias) {
+  static const bool off = [] {
+    const char* e = std::getenv("SDPA_DECODE");
+    return e && e[0] == '0';
+  }();
+  return !off && p->dtype != SDPA_F32 && !has_bias && p->dropout_probability == 0.f &&
+         p->s_q <= sdpa::kDecodeMaxSq;
+}
+// Workgroups the split-KV plan aims for (SDPA_DECODE_WGS overrides).
+int64_t decode_target_wgs() {
+  static const int64_t n = [] {
+    const char* e = std::getenv("SDPA_DECODE_WGS");
+    const long long v = e ? std::atoll(e) : 0;
+    return v > 0 ? (int64_t)v : (int64_t)256;
+  }();
+  return n;
+}
+sdpa::DecodePlan decode_plan(const sdpa_problem_t* p) {
+  return sdpa::plan_decode(p->b, p->h, kv_group(p), p->s_q, p->s_kv, decode_target_wgs());
+}
+// split-KV partials: O [ns][B H s_q][d_v] fp32, then LSE [ns][B H s_q]
+size_t decode_part_o_bytes(const sdpa_problem_t* p, const sdpa::DecodePlan& pl) {
+  return align_up(sizeof(float) * (size_t)pl.ns * (size_t)p->b * (size_t)p->h * (size_t)p->s_q *
+                  (size_t)p->d_v);
+}
+size_t decode_workspace_bytes(const sdpa_problem_t* p, const sdpa::DecodePlan& pl) {
+  if (pl.ns <= 1) return 0;
+  return decode_part_o_bytes(p, pl) +
+         align_up(sizeof(float) * (size_t)pl.ns * (size_t)p->b * (size_t)p->h * (size_t)p->s_q);
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,8 +227,8 @@ const char* sdpa_status_string(sdpa_status_t st) {
 const char* sdpa_last_error_message(void) { return g_msg; }
 
 size_t sdpa_fwd_workspace_size(const sdpa_problem_t* p) {
-  (void)p;
-  return 0;
+  if (check_problem(p) != SDPA_OK || empty_problem(p) || !decode_eligible(p, false)) return 0;
+  return decode_workspace_bytes(p, decode_plan(p));
 }
 
 size_t sdpa_bwd_workspace_size(const sdpa_problem_t* p) {
@@ -211,8 +244,6 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
-  (void)workspace;
-  (void)workspace_bytes;
   if (empty_problem(p)) return SDPA_OK;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
@@ -245,8 +276,34 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
                  "bias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b, (long long)p->h,
                  (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk, (long long)p->d_v,
                  p->is_causal, attn_bias != nullptr, (double)p->dropout_probability, group);
-  hipError_t e = sdpa::launch_fwd(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a,
-                                  (hipStream_t)stream);
+  hipError_t e;
+  if (decode_eligible(p, attn_bias != nullptr)) {
+    // thin query: split-KV when the workspace holds the partials, else one
+    // split per (batch, key/value head, row group)
+    sdpa::DecodePlan pl = decode_plan(p);
+    const size_t need = decode_workspace_bytes(p, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16 != 0)) {
+      pl.chunk = (int32_t)((p->s_kv + 127) / 128 * 128);
+      pl.ns = 1;
+    }
+    sdpa::DecodeArgs d{};
+    d.ns = pl.ns;
+    d.chunk = pl.chunk;
+    d.rg = pl.rg;
+    d.nr = p->b * p->h * p->s_q;
+    if (pl.ns > 1) {
+      d.part_o = (float*)workspace;
+      d.part_lse = (float*)((char*)workspace + decode_part_o_bytes(p, pl));
+    }
+    if (log_on())
+      std::fprintf(stderr, "[sdpa] fwd thin-query path: splits=%d chunk=%d row_groups=%d\n", d.ns,
+                   d.chunk, d.rg);
+    e = sdpa::launch_fwd_decode(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a, d,
+                                (hipStream_t)stream);
+  } else {
+    e = sdpa::launch_fwd(io(p->dtype), (int)p->d_qk, (int)p->d_v, banded(p), a,
+                         (hipStream_t)stream);
+  }
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
 }

@@ -1,0 +1,348 @@
+// Thin-query forward (decode): few query rows per sequence, long key/value
+// sequences, no bias and no dropout.
+//
+// The same O = softmax(scale * Q K^T, masked) V and natural-log LSE as the
+// main forward, organised for the shape where it is bound by streaming K and
+// V from HBM rather than by the matrix cores:
+//   - the query rows of every query head that shares one key/value head are
+//     packed into the same 32-row MFMA tile (oneDNN "SDPA primitive"
+//     execute_forward batches a single-query problem over the key/value
+//     heads so that several query heads share one workgroup), so K and V are
+//     read once per key/value head instead of once per query head;
+//   - the key range is split over workgroups (split-KV), so that a handful
+//     of (batch, key/value head) pairs still fills the chip; each split
+//     writes a normalised partial O and its LSE, and a second kernel merges
+//     them with weights exp(LSE_split - LSE);
+//   - inside a workgroup the four waves stream disjoint 32-key tiles into
+//     their own double-buffered LDS tiles (no workgroup barrier in the
+//     loop) and merge their running (max, sum, O) once at the end.  A wave
+//     copies its current tile's operands into registers first and at once
+//     reuses the buffer for the tile after next, so two tiles per wave are
+//     in flight while it computes (the chip needs several MB in flight to
+//     cover HBM latency, and LDS only holds two buffers per wave).
+// Per 32-key tile a wave computes S^T = K Q^T and O^T += V^T P^T exactly as
+// the main forward does (sig-permuted K rows, transposing LDS reads of V),
+// with the same base-2 online softmax and lazy rescale.
+#include <algorithm>
+
+#include "sdpa_kcommon.h"
+
+namespace sdpa {
+
+template <typename T, int DQK, int DV, bool BAND>
+__global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const DecodeArgs d) {
+  constexpr int BC = 32;        // keys per wave tile
+  constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
+  constexpr int DB = DV / 32;   // 32-wide blocks of d_v
+  constexpr float TAU = 8.f;
+  // per wave: two K and two V tiles; after the loop the wave's K region
+  // holds its partial O (32 x DV fp32) and its V region its row max / sum
+  static_assert(2 * BC * DQK * sizeof(T) >= 32 * DV * sizeof(float), "O partial must fit");
+  __shared__ __attribute__((aligned(1024))) T sK[4][2][BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sV[4][2][BC * DV];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = wave_id();
+  const int Hkv = a.H / a.G;
+  // XCD x = id mod 8 owns a contiguous range of the (batch, kv head, split,
+  // row group) units, row groups innermost (they read the same K/V)
+  const int64_t n_units = (int64_t)a.B * Hkv * d.ns * d.rg;
+  const int64_t per_xcd = (n_units + 7) / 8;
+  const int64_t pos = blockIdx.x >> 3;
+  const int64_t u = (int64_t)(blockIdx.x & 7) * per_xcd + pos;
+  if (pos >= per_xcd || u >= n_units) return;
+  const int rg = (int)(u % d.rg);
+  const int split = (int)((u / d.rg) % d.ns);
+  const int hk = (int)((u / ((int64_t)d.rg * d.ns)) % Hkv);
+  const int b = (int)(u / ((int64_t)d.rg * d.ns * Hkv));
+  const SeqPos sp = resolve_seq(a.seq, b);
+  const int sq = sp.sq, skv = sp.skv;
+  const int nrows = a.G * sq;  // (query head of the group, position) pairs
+  const int r0 = 32 * rg;
+  if (r0 >= nrows) return;
+
+  // this lane's row: query head hk*G + gi, position s
+  const int r = r0 + l32;
+  const bool row_ok = r < nrows;
+  const int gi = row_ok ? r / sq : 0;
+  const int s_pos = row_ok ? r - gi * sq : 0;
+  const int h = hk * a.G + gi;
+
+  // positions covered by the workgroup's rows, and the keys they can see
+  const int r1 = min(r0 + 32, nrows) - 1;
+  const bool one_head = r0 / sq == r1 / sq;
+  const int s_lo = one_head ? r0 % sq : 0, s_hi = one_head ? r1 % sq : sq - 1;
+  const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
+  const int k_begin = BAND ? (int)max((int64_t)0, (int64_t)s_lo + bd.lo) : 0;
+  const int k_end = BAND ? (int)min((int64_t)skv, (int64_t)s_hi + bd.hi + 1) : skv;
+  // this split's keys, in 32-key tiles; wave w takes tiles tb + w + 4j
+  const int ks = max(k_begin, (int)min((int64_t)split * d.chunk, (int64_t)skv));
+  const int ke = min(k_end, (int)min((int64_t)(split + 1) * d.chunk, (int64_t)skv));
+  const int tb = ks / BC;
+  const int te = ke > ks ? (ke + BC - 1) / BC : tb;
+  const int ntw = te - tb > w ? (te - tb - w + 3) / 4 : 0;
+
+  // Q first: loads complete in issue order, so waiting for Q does not wait
+  // for the K/V tiles behind it
+  const T* qrow = base_ptr<T>(a.q, a.sq_, sp, h, true) + (int64_t)s_pos * a.sq_.s;
+  u32x4 qreg[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+    qreg[t] = row_ok ? *(const u32x4*)(qrow + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+
+  TileLoader<DQK, BC, T, 1> ldK;
+  TileLoader<DV, BC, T, 1> ldV;
+  ldK.init(base_ptr<T>(a.k, a.sk_, sp, hk, false), a.sk_.s, 0, lane);
+  ldV.init(base_ptr<T>(a.v, a.sv_, sp, hk, false), a.sv_.s, 0, lane);
+  if (ntw > 0) {
+    ldK.load(sK[w][0], (tb + w) * BC, skv, 0, lane);
+    ldV.load(sV[w][0], (tb + w) * BC, skv, 0, lane);
+  }
+  if (ntw > 1) {
+    ldK.load(sK[w][1], (tb + w + 4) * BC, skv, 0, lane);
+    ldV.load(sV[w][1], (tb + w + 4) * BC, skv, 0, lane);
+  }
+  // loads of one tile (K and V), all direct-to-LDS
+  constexpr int TILE_LOADS = TileLoader<DQK, BC, T, 1>::PER_WAVE + TileLoader<DV, BC, T, 1>::PER_WAVE;
+
+  const float c = a.scale_log2;
+  // a zero scale cannot hide a score with an infinity through the FMA: such
+  // tiles use raw scores 0 (visible) / -inf (hidden) and an effective scale 1
+  const bool zs = c == 0.f;
+  const float ce = zs ? 1.f : c;
+  const bool pos_scale = ce >= 0.f;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;  // m_run in scaled log2 units
+
+  RowReader<DQK, T> rdK;
+  TrReader<DV, T> rdV;
+  rdK.init(lane);
+  rdV.init(lane);
+
+  // Tile j sits in buffer j % 2 (`cK`, `cV`); tile j + 1, if any, is in
+  // flight into the other buffer.
+  auto tile = [&](int j, T* cK, T* cV) __attribute__((always_inline)) {
+    const int n0 = (tb + w + 4 * j) * BC;
+    // tile j has landed (tile j + 1 may still be loading)
+    if (j + 1 < ntw) wait_vm<TILE_LOADS>();
+    else wait_vm<0>();
+    u32x4 kop[KT], vop[2 * DB];
+    static_for<KT>([&](auto t) __attribute__((always_inline)) { kop[t] = rdK.template read<t>(cK, 0); });
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      static_for<DB>([&](auto db) __attribute__((always_inline)) {
+        vop[tt * DB + db] = rdV.template read<32 * db>(cV, 16 * tt);
+      });
+    if (j + 2 < ntw) {
+      wait_lds();  // the operands are in registers: the buffers are free
+      ldK.load(cK, n0 + 8 * BC, skv, 0, lane);
+      ldV.load(cV, n0 + 8 * BC, skv, 0, lane);
+    }
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) s = mfma32<T>(kop[t], qreg[t], s);
+
+    // masked unless every key of the tile is visible from every position
+    const bool need_mask =
+        (n0 + BC > skv) || (BAND && !(n0 - s_hi >= bd.lo && n0 + BC - 1 - s_lo <= bd.hi));
+    auto visible = [&](int rr) {
+      const int kv = n0 + 16 * (rr >> 3) + 8 * g + (rr & 7);
+      return kv < skv && (!BAND || (kv - s_pos >= bd.lo && kv - s_pos <= bd.hi));
+    };
+    const float hide = pos_scale ? -INFINITY : INFINITY;
+    if (need_mask || zs) {
+      keep_branch();
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[rr] = visible(rr) ? (zs ? 0.f : s[rr]) : hide;
+    }
+    float mrow;
+    if (pos_scale) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
+      mx = max_pair32(mx);
+      mrow = mx == -INFINITY ? -INFINITY : mx * ce;
+    } else {
+      float mn = INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mn = fminf(mn, s[rr]);
+      mn = -max_pair32(-mn);
+      mrow = mn == INFINITY ? -INFINITY : mn * ce;
+    }
+
+    const float m_new = fmaxf(m_run, mrow);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
+      keep_branch();
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      u32x4 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * tt + 2 * e], ce, -m_run));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * tt + 2 * e + 1], ce, -m_run));
+        psum += x0 + x1;
+        pb[e] = pack2<T>(x0, x1);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb, oacc[db]);
+    }
+    l_run += psum;
+  };
+
+  for (int j = 0; j < ntw; j += 2) {
+    tile(j, sK[w][0], sV[w][0]);
+    if (j + 1 < ntw) tile(j + 1, sK[w][1], sV[w][1]);
+  }
+
+  // ---- merge the four waves' (max, sum, O) through LDS -----------------
+  wait_all();
+  // [32 rows][DV] with 16-byte chunks XOR-swizzled by row (conflict-free
+  // column writes)
+  float* sOw = (float*)sK[w][0];
+  float* sMLw = (float*)sV[w][0];  // [32] max, then [32] sum
+  const float l_row = sum_pair32(l_run);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int dd = 32 * db + 8 * rr + 4 * g;
+      *(f32x4*)(sOw + l32 * DV + ((((dd >> 2) ^ l32) & (DV / 4 - 1)) << 2)) =
+          f32x4{oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
+    }
+  if (g == 0) {
+    sMLw[l32] = m_run;
+    sMLw[32 + l32] = l_row;
+  }
+  __syncthreads();
+
+  const int64_t st_group_rows = a.seq.cu_q ? a.seq.cu_q[a.B] : 0;
+  for (int e = tid; e < 32 * DV; e += 256) {
+    const int rl = e / DV, dd = e - rl * DV;
+    const int rr_ = r0 + rl;
+    if (rr_ >= nrows) break;  // rows are contiguous: the rest are past the end too
+    float M = -1e30f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, ((const float*)sV[v][0])[rl]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float* ml = (const float*)sV[v][0];
+      const float f = __builtin_amdgcn_exp2f(ml[rl] - M);
+      L += f * ml[32 + rl];
+      O += f * ((const float*)sK[v][0])[rl * DV + ((((dd >> 2) ^ rl) & (DV / 4 - 1)) << 2) + (dd & 3)];
+    }
+    const float o = L > 0.f ? O / L : 0.f;
+    const float lse = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    const int gr = rr_ / sq, sr = rr_ - gr * sq, hr = hk * a.G + gr;
+    const int64_t st = row_stat_base(a.seq, sp, b, hr, a.H, st_group_rows) + sr;
+    if (d.ns == 1) {
+      T* orow = base_ptr_mut<T>(a.o, a.so_, sp, hr, true) + (int64_t)sr * a.so_.s;
+      st_elem<T>(orow + dd, o);
+      if (a.lse && dd == 0) a.lse[st] = lse;
+    } else {
+      d.part_o[((int64_t)split * d.nr + st) * DV + dd] = o;
+      if (dd == 0) d.part_lse[(int64_t)split * d.nr + st] = lse;
+    }
+  }
+}
+
+// Merge the splits of one row per wave: LSE = log sum_i exp(LSE_i), O = sum_i
+// exp(LSE_i - LSE) O_i, in ascending split order.
+template <typename T, int DV>
+__global__ void __launch_bounds__(256) fwd_decode_combine(const FwdArgs a, const DecodeArgs d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t st = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the row's output address: batch rows are ((b H + h) s_q + s), group rows
+  // (h T + token)
+  T* orow;
+  if (a.seq.cu_q) {
+    const int64_t T_ = a.seq.cu_q[a.B];
+    if (st >= (int64_t)a.H * T_) return;
+    const int64_t h = st / T_, tok = st - h * T_;
+    orow = (T*)a.o + h * a.so_.h + tok * a.so_.s;
+  } else {
+    if (st >= d.nr) return;
+    const int64_t bh = st / a.seq.s_q, s = st - bh * a.seq.s_q;
+    const int64_t b = bh / a.H, h = bh - b * a.H;
+    orow = (T*)a.o + b * a.so_.b + h * a.so_.h + s * a.so_.s;
+  }
+  float M = -INFINITY;
+  for (int i = 0; i < d.ns; ++i) M = fmaxf(M, d.part_lse[(int64_t)i * d.nr + st]);
+  constexpr int PER = (DV + 63) / 64;
+  float acc[PER], L = 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < d.ns; ++i) {
+      const float f = __builtin_amdgcn_exp2f((d.part_lse[(int64_t)i * d.nr + st] - M) * kLog2e);
+      L += f;
+      const float* po = d.part_o + ((int64_t)i * d.nr + st) * DV;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if (lane + 64 * k < DV) acc[k] += f * po[lane + 64 * k];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if (lane + 64 * k < DV) st_elem<T>(orow + lane + 64 * k, acc[k] * inv);
+  if (a.lse && lane == 0) a.lse[st] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+DecodePlan plan_decode(int64_t B, int64_t H, int32_t G, int64_t s_q, int64_t s_kv,
+                       int64_t target_wgs) {
+  DecodePlan pl;
+  pl.rg = (int32_t)((G * s_q + 31) / 32);
+  const int64_t units = B * (H / G) * pl.rg;
+  // enough splits to give about target_wgs workgroups, but at least 256
+  // keys (two tiles per wave) per split
+  int64_t ns = units > 0 ? (target_wgs + units - 1) / units : 1;
+  ns = std::max<int64_t>(1, std::min(ns, (s_kv + 255) / 256));
+  int64_t chunk = (s_kv + ns - 1) / ns;
+  chunk = (chunk + 127) / 128 * 128;
+  pl.chunk = (int32_t)chunk;
+  pl.ns = (int32_t)((s_kv + chunk - 1) / chunk);
+  return pl;
+}
+
+template <typename T, int DQK, int DV>
+static hipError_t decode_dims(bool band, const FwdArgs& a, const DecodeArgs& d, hipStream_t st) {
+  const int64_t units = (int64_t)a.B * (a.H / a.G) * d.ns * d.rg;
+  dim3 grid((unsigned)(8 * ((units + 7) / 8))), block(256);
+  if (band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true>), grid, block, 0, st, a, d);
+  else hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false>), grid, block, 0, st, a, d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || d.ns == 1) return e;
+  dim3 cgrid((unsigned)((d.nr + 3) / 4));
+  hipLaunchKernelGGL((fwd_decode_combine<T, DV>), cgrid, block, 0, st, a, d);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t decode_type(int dqk, int dv, bool band, const FwdArgs& a, const DecodeArgs& d,
+                              hipStream_t st) {
+  if (dqk == 64 && dv == 64) return decode_dims<T, 64, 64>(band, a, d, st);
+  if (dqk == 128 && dv == 128) return decode_dims<T, 128, 128>(band, a, d, st);
+  if (dqk == 192 && dv == 128) return decode_dims<T, 192, 128>(band, a, d, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_decode(IoType t, int dqk, int dv, bool band, const FwdArgs& a,
+                             const DecodeArgs& d, hipStream_t st) {
+  if (t == IoType::BF16) return decode_type<__bf16>(dqk, dv, band, a, d, st);
+  if (t == IoType::F16) return decode_type<_Float16>(dqk, dv, band, a, d, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

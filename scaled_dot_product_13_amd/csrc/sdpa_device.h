@@ -179,6 +179,19 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // Wait for all of this wave's outstanding memory operations (including the
 // direct-to-LDS loads) to complete; a barrier after it publishes the tile.
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until at most N vector memory operations of this wave are
+// outstanding (they complete in issue order), leaving the LDS and export
+// counters alone: gfx9 s_waitcnt packs vmcnt[3:0] at bits 3:0 and vmcnt[5:4]
+// at bits 15:14, with expcnt (bits 6:4) and lgkmcnt (bits 11:8) at their
+// no-wait maxima.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait for every outstanding LDS read of this wave.
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
 
 // v ^ K as one v_xor_b32 that the compiler can neither hoist out of a loop
 // nor merge with another: LDS offsets formed this way are recomputed at

@@ -71,6 +71,27 @@ struct BwdArgs {
   DropoutArgs drop;
 };
 
+// Thin-query forward (split-KV).  Each split of the keys writes a normalised
+// partial O and its natural-log LSE for every row, at row index st (the
+// dense stats index: batch (b H + h) s_q + s, group h T + token) of slice
+// `split`; a combine kernel merges them.  With ns == 1 the kernel writes O
+// and LSE itself and no partials are used.
+struct DecodeArgs {
+  float* part_o;    // [ns][nr][d_v]
+  float* part_lse;  // [ns][nr]
+  int64_t nr;       // rows per slice: B * H * s_q
+  int32_t ns;       // splits
+  int32_t chunk;    // keys per split, a multiple of 128
+  int32_t rg;       // 32-row groups of (query head of the group, position) pairs
+};
+struct DecodePlan {
+  int32_t ns, chunk, rg;
+};
+// Splits for about `target_wgs` workgroups over B x (H / G) x row groups.
+DecodePlan plan_decode(int64_t B, int64_t H, int32_t G, int64_t s_q, int64_t s_kv,
+                       int64_t target_wgs);
+constexpr int64_t kDecodeMaxSq = 16;  // thin-query path: s_q <= 16
+
 // Launchers (each returns hipSuccess or the launch error).  `causal`,
 // `bias` and `dropout` select template instances.
 hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a,
@@ -82,6 +103,8 @@ hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs
 // from o, dout and lse (16-bit io only)
 hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a,
                          hipStream_t st, bool with_pre = false);
+hipError_t launch_fwd_decode(IoType t, int dqk, int dv, bool band, const FwdArgs& a,
+                             const DecodeArgs& d, hipStream_t st);
 bool mfma_dims_supported(int dqk, int dv);
 
 }  // namespace sdpa

@@ -66,6 +66,13 @@ WORKLOADS = {
 }
 
 
+# Thin-query (decode) workload: one new token per sequence attending to a
+# long key/value cache, grouped-query heads (4 query heads per key/value
+# head), bottom-right causal as a decoder step is.
+DECODE = Workload("bf16 decode B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1, 8192, 128, 128,
+                  causal=True, bottom_right=True, h_kv=8, seed=1006)
+
+
 def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
     """Draw the workload's tensors on the CPU.  Returns a dict with
     q, k, v, dout, [bias], [lengths, cu_seqlens, max_seqlen and their _kv

@@ -175,8 +175,11 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
 def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
              seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
              max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None,
-             bottom_right=False, window_left=None, window_right=None):
-    """Forward.  Returns (o, lse or None, keep or None)."""
+             bottom_right=False, window_left=None, window_right=None, split_kv=True,
+             workspace=None):
+    """Forward.  Returns (o, lse or None, keep or None).  split_kv=False
+    passes no workspace, so a thin-query problem runs unsplit; `workspace`
+    (uint8, at least fwd_workspace_size bytes) avoids an allocation."""
     group = cu_seqlens_q is not None
     p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
                      offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
@@ -193,8 +196,11 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
     keep = None
     if return_keep:
         keep = torch.zeros((p.b, p.h, p.s_q, p.s_kv), dtype=torch.uint8, device=q.device)
-    ws_n = _lib.sdpa_fwd_workspace_size(ctypes.byref(p))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
+    ws_n = _lib.sdpa_fwd_workspace_size(ctypes.byref(p)) if split_kv else 0
+    if workspace is not None and workspace.numel() >= ws_n:
+        ws = workspace
+    else:
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device) if ws_n else None
     _check(_lib.sdpa_fwd(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
                          _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),
                          _ptr(out), _strides(out, group), _ptr(lse if return_lse else None),
@@ -227,6 +233,12 @@ def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, drop
                          _ptr(dv), _strides(dv, group), _ptr(dbias), _strides(dbias, False),
                          _ptr(workspace), workspace.numel(), _stream()))
     return dq, dk, dv, dbias
+
+
+def fwd_workspace_size(q, k, v, **kw):
+    """Bytes of forward workspace for these tensors and options (see
+    make_problem); nonzero only for split-KV thin-query problems."""
+    return _lib.sdpa_fwd_workspace_size(ctypes.byref(make_problem(q, k, v, **kw)))
 
 
 def stats_layout(b, h, s_q):

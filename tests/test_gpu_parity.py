@@ -97,7 +97,7 @@ def _mask_kw(wl):
 
 
 def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd",
-                 kv_lengths=None):
+                 kv_lengths=None, fwd_kw=None):
     """Run fwd+bwd on the GPU and compare with the oracle on `heads`
     (all heads when None).  Returns the max errors."""
     x = inputs.make_inputs(wl, lengths, kv_lengths)
@@ -119,7 +119,7 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
     _say(wl.name, wl.dtype, "B", wl.b, "H", wl.h, "Sq", wl.s_q, "Skv", wl.s_kv, "d", wl.d_qk,
          wl.d_v, "causal", wl.causal, "bias", wl.bias, "p", wl.dropout_p, "group", group, layout,
          "mask", _mask_kw(wl))
-    o, lse, keep = S.sdpa_fwd(gq, gk, gv, bias=gb, return_keep=want_keep, **kw)
+    o, lse, keep = S.sdpa_fwd(gq, gk, gv, bias=gb, return_keep=want_keep, **kw, **(fwd_kw or {}))
     dq, dk, dv, dbias = S.sdpa_bwd(gq, gk, gv, o, gdo, lse, bias=gb, want_dbias=bias is not None, **kw)
     torch.cuda.synchronize()
 
@@ -265,6 +265,67 @@ def test_mask_grouped_query_window(S):
     wl = inputs.small("f16", b=1, h=4, h_kv=1, s_q=260, s_kv=260, d_qk=128, d_v=128, causal=False,
                       bias=True, seed=23, window_left=40, window_right=70)
     run_workload(S, wl)
+
+
+# Thin-query problems (s_q <= 16, 16-bit io, no bias or dropout) run the
+# split-KV forward; split=False runs the same kernel unsplit.
+THIN_Q = [
+    # dtype, dims, s_q, s_kv, h, h_kv, causal, bottom_right, window_left, split
+    ("bf16", (128, 128), 1, 1000, 8, 2, False, False, None, True),
+    ("bf16", (128, 128), 1, 1000, 8, 2, False, False, None, False),
+    ("bf16", (128, 128), 4, 777, 8, 2, True, True, None, True),
+    ("f16", (64, 64), 16, 2081, 16, 2, True, True, None, True),  # 4 row groups per K/V head
+    ("f16", (192, 128), 3, 500, 3, 3, True, True, 100, True),
+    ("bf16", (128, 128), 8, 300, 4, 4, True, False, None, True),  # top-left: row i sees j <= i
+    ("bf16", (64, 64), 1, 17, 4, 1, False, False, None, True),
+    ("bf16", (128, 128), 16, 5, 4, 2, True, True, None, True),  # rows without keys
+    ("bf16", (128, 128), 1, 4096, 4, 4, True, True, 100, True),  # most splits see no key
+    ("f16", (128, 128), 5, 3000, 6, 3, False, False, None, True),
+]
+
+
+@pytest.mark.parametrize("case", THIN_Q, ids=lambda c: f"{c[0]}-d{c[1][0]}-{c[2]}x{c[3]}-h{c[4]}kv{c[5]}"
+                         f"-c{int(c[6])}-br{int(c[7])}-w{c[8]}-split{int(c[9])}")
+def test_thin_query_parity(S, case):
+    dt, (dq_, dv_), sq, skv, h, hkv, causal, br, wl_, split = case
+    wl = inputs.small(dt, b=2, h=h, h_kv=hkv, s_q=sq, s_kv=skv, d_qk=dq_, d_v=dv_, causal=causal,
+                      seed=sq * 11 + skv, bottom_right=br, window_left=wl_)
+    run_workload(S, wl, fwd_kw=dict(split_kv=split))
+
+
+@pytest.mark.parametrize("lengths,kv_lengths", [([1, 1, 1, 1], [1, 700, 3000, 64]),
+                                                ([2, 5, 1, 16], [40, 1000, 1, 300])])
+def test_thin_query_varlen(S, lengths, kv_lengths):
+    wl = inputs.small("bf16", b=len(lengths), h=8, h_kv=2, d_qk=128, d_v=128, causal=True,
+                      bottom_right=True, seed=29, varlen=(len(lengths), 1, 16))
+    run_workload(S, wl, lengths=lengths, kv_lengths=kv_lengths)
+
+
+def test_thin_query_zero_scale(S):
+    # every visible score equal: O is the mean of the visible V rows
+    wl = inputs.small("bf16", b=1, h=4, h_kv=2, s_q=2, s_kv=600, scale=0.0, causal=True,
+                      bottom_right=True, window_left=300, seed=31)
+    run_workload(S, wl)
+
+
+def test_decode_workload_full(S):
+    """The decode workload at full size, forward only, every row against the
+    oracle."""
+    wl = inputs.DECODE
+    x = inputs.make_inputs(wl)
+    _say(wl.name)
+    g = [x[n].cuda() for n in ("q", "k", "v")]
+    kw = dict(scale=wl.softmax_scale, causal=wl.causal, bottom_right=wl.bottom_right)
+    o, lse, _ = S.sdpa_fwd(*g, **kw)
+    o1, lse1, _ = S.sdpa_fwd(*g, split_kv=False, **kw)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.double().numpy()
+    ref = O.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale=wl.softmax_scale, causal=True,
+                bottom_right=True)
+    for got_o, got_lse in ((o, lse), (o1, lse1)):
+        _cmp("o", _np(got_o), ref["o"], x["dtype"])
+        _cmp("lse", _np(got_lse), ref["lse"], x["dtype"])
+    _say("max |o - ref|", float(np.max(np.abs(_np(o) - ref["o"]))))
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
