@@ -36,6 +36,12 @@
  *     unbounded when not given), and causal meaning hi <= 0.
  *   - A row with no visible key has O_i = 0, LSE_i = -inf and zero gradients
  *     (oneDNN's softmax_inf_as_zero flag).
+ *   - ALiBi (CK's FmhaBwdAlibiKargs: one fp32 slope per batch and head, and
+ *     the position encoding built in FmhaBwdDQDKDVKernel's operator() from
+ *     the mask, or bottom-right aligned when there is no mask) adds
+ *       -slope * |j - i - off|
+ *     to s_ij, with off the mask's alignment (s_kv - s_q bottom-right, 0
+ *     top-left; s_kv - s_q without a mask).  It takes the place of Bias.
  *   - Dropout multiplies the normalised P after the row statistics are taken;
  *     LSE comes from the undropped P (CK's init_dropout keeps 1/(1-p) as the
  *     rescale and passes the undropped probability to the D preprocess).
@@ -138,6 +144,10 @@ typedef struct {
      * oneDNN's top-left and bottom-right causal kinds). */
     int32_t band;
     int64_t band_off, band_lo, band_hi;
+    /* ALiBi (when alibi != 0): s_ij += -alibi_slope * |j - i - alibi_off| */
+    int32_t alibi;
+    double alibi_slope;
+    int64_t alibi_off;
 } oracle_head_t;
 
 /* Visible keys of row i: the contiguous range [*first, *last]; empty when
@@ -167,6 +177,7 @@ static double row_probs(const oracle_head_t *h, int64_t i, double *s) {
         double acc = 0.0;
         for (int64_t c = 0; c < h->dqk; ++c) acc += qi[c] * kj[c];
         s[j] = h->scale * acc + (h->bias ? h->bias[i * h->ld_bias + j] : 0.0);
+        if (h->alibi) s[j] -= h->alibi_slope * fabs((double)(j - i - h->alibi_off));
     }
     double m = -INFINITY;
     for (int64_t j = first; j <= last; ++j)

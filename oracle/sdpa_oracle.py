@@ -47,6 +47,8 @@ class _Head(ctypes.Structure):
         ("keep", ctypes.POINTER(ctypes.c_uint8)), ("ld_keep", ctypes.c_int64),
         ("band", ctypes.c_int32), ("band_off", ctypes.c_int64),
         ("band_lo", ctypes.c_int64), ("band_hi", ctypes.c_int64),
+        ("alibi", ctypes.c_int32), ("alibi_slope", ctypes.c_double),
+        ("alibi_off", ctypes.c_int64),
     ]
 
 
@@ -119,7 +121,7 @@ def _band(causal, bottom_right, window_left, window_right):
 
 
 def _heads(q, k, v, bias, dout, outs, *, scale, causal, p_drop, seed, offset,
-           cu_q, cu_kv, select, band=None, bottom_right=False):
+           cu_q, cu_kv, select, band=None, bottom_right=False, alibi=None):
     """Build the list of head descriptors for batch or varlen layout."""
     heads = []
     keep = outs.get("keep")
@@ -177,6 +179,13 @@ def _heads(q, k, v, bias, dout, outs, *, scale, causal, p_drop, seed, offset,
                 hd.dv_out, hd.ld_dv = _ptr(outs["dv"], (sk0 * H + h) * Dv), H * Dv
             hd.bh = b * H + h
             heads.append(hd)
+    if alibi is not None:
+        # (slopes [B, H], alignment bottom-right?) for each head descriptor
+        slopes, align_br = alibi
+        for hd, (b, h) in zip(heads, pairs):
+            hd.alibi = 1
+            hd.alibi_slope = float(slopes[b, h])
+            hd.alibi_off = hd.skv - hd.sq if align_br else 0
     for hd in heads:
         hd.scale = float(scale)
         hd.causal = 1 if causal else 0
@@ -188,6 +197,22 @@ def _heads(q, k, v, bias, dout, outs, *, scale, causal, p_drop, seed, offset,
         hd.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
         hd.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
     return heads
+
+
+def _alibi(alibi_slopes, n_batch, n_heads, causal, bottom_right, window_left, window_right):
+    """(slopes [B, H], bottom-right alignment) for the ALiBi term, or None.
+    A slope vector [H] is shared by every batch entry.  The alignment is the
+    mask's (bottom-right or top-left) and bottom-right when there is no mask,
+    as CK builds its position encoding from the mask or, without one, from
+    the bottom-right corner."""
+    if alibi_slopes is None:
+        return None
+    sl = np.asarray(alibi_slopes, dtype=np.float64)
+    if sl.ndim == 1:
+        sl = np.broadcast_to(sl, (n_batch, n_heads))
+    assert sl.shape == (n_batch, n_heads)
+    masked = causal or window_left is not None or window_right is not None
+    return sl, (bottom_right or not masked)
 
 
 def _run(fn, heads, threads):
@@ -232,11 +257,13 @@ def _sum_groups(t, r, complete):
 
 def fwd(q, k, v, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0,
         cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_keep=False,
-        bottom_right=False, window_left=None, window_right=None):
+        bottom_right=False, window_left=None, window_right=None, alibi_slopes=None):
     """Forward definition.  Returns dict(o=..., lse=..., [keep=...]).
     k and v may have fewer heads than q (grouped-query attention).  The mask
     is top-left causal, or with bottom_right / window_left / window_right the
-    band lo <= j - i - off <= hi described in the C source."""
+    band lo <= j - i - off <= hi described in the C source.  alibi_slopes
+    ([B, H] or [H]) adds -slope |j - i - off| to the scores in place of a
+    bias (see _alibi for the alignment)."""
     q, k, v, bias = _as64(q), _as64(k), _as64(v), _as64(bias)
     r = _kv_ratio(q, k, cu_seqlens_q is not None)
     k, v = np.ascontiguousarray(_repeat_kv(k, r)), np.ascontiguousarray(_repeat_kv(v, r))
@@ -254,14 +281,16 @@ def fwd(q, k, v, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0
     hs = _heads(q, k, v, bias, None, outs, scale=scale, causal=causal, p_drop=p_drop,
                 seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads,
                 band=_band(causal, bottom_right, window_left, window_right),
-                bottom_right=bottom_right)
+                bottom_right=bottom_right,
+                alibi=_alibi(alibi_slopes, q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1,
+                             q.shape[1], causal, bottom_right, window_left, window_right))
     _run("oracle_fwd", hs, threads)
     return outs
 
 
 def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, offset=0,
         cu_seqlens_q=None, cu_seqlens_kv=None, heads=None, threads=0, want_dbias=None,
-        bottom_right=False, window_left=None, window_right=None):
+        bottom_right=False, window_left=None, window_right=None, alibi_slopes=None):
     """Backward definition (recomputes O and LSE itself).
 
     Returns dict(o, lse, D, dq, dk, dv[, dbias]).  With fewer key/value heads
@@ -291,7 +320,9 @@ def bwd(q, k, v, dout, *, scale, causal=False, bias=None, p_drop=0.0, seed=0, of
     hs = _heads(q, k, v, bias, dout, outs, scale=scale, causal=causal, p_drop=p_drop,
                 seed=seed, offset=offset, cu_q=cu_seqlens_q, cu_kv=cu_seqlens_kv, select=heads,
                 band=_band(causal, bottom_right, window_left, window_right),
-                bottom_right=bottom_right)
+                bottom_right=bottom_right,
+                alibi=_alibi(alibi_slopes, q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1,
+                             q.shape[1], causal, bottom_right, window_left, window_right))
     _run("oracle_bwd", hs, threads)
     if r > 1:
         nb = q.shape[0] if cu_seqlens_q is None else len(cu_seqlens_q) - 1

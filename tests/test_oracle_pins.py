@@ -11,6 +11,10 @@ Every test here runs on the CPU.  What pins what:
     oracle's own forward, torch float64 autograd of the forward, and
     invariants (row sums of dS vanish, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
   - group mode: equals batch mode run sequence by sequence.
+  - ALiBi: slope 0 is the plain forward; a very steep slope leaves only the
+    key on the aligned diagonal (O_i = V_{i+off}); under a top-left causal
+    mask it equals a per-key bias slope * j (the -slope * i part is constant
+    along a row and cancels in the softmax); central differences.
   - mutation check: deliberately broken builds of the oracle fail the pins.
 """
 import math
@@ -425,6 +429,75 @@ def test_backward_invariants(p):
     assert np.allclose(g["lse"], f["lse"], atol=0, rtol=0)
 
 
+# ----------------------------------------------------------------- ALiBi ----
+def test_alibi_zero_slope_is_the_plain_forward():
+    B, H, Sq, Skv, D = 2, 3, 9, 13, 8
+    q, k, v = _rand((B, H, Sq, D), 201), _rand((B, H, Skv, D), 202), _rand((B, H, Skv, D), 203)
+    for kw in (dict(), dict(causal=True), dict(causal=True, bottom_right=True, window_left=3)):
+        a = O.fwd(q, k, v, scale=0.4, alibi_slopes=np.zeros((B, H)), **kw)
+        b = O.fwd(q, k, v, scale=0.4, **kw)
+        assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"]), kw
+
+
+@pytest.mark.parametrize("causal,bottom_right,sq,skv", [(False, False, 7, 12), (True, False, 9, 9),
+                                                       (True, True, 6, 11), (False, False, 10, 10)])
+def test_alibi_steep_slope_keeps_only_the_diagonal_key(causal, bottom_right, sq, skv):
+    # with slope >> |scores| every row's weight sits on the key j = i + off:
+    # bottom-right without a mask (off = s_kv - s_q), the mask's alignment
+    # otherwise
+    B, H, D = 1, 2, 5
+    q, k, v = _rand((B, H, sq, D), 211, 0.1), _rand((B, H, skv, D), 212, 0.1), _rand((B, H, skv, D), 213)
+    slope = 80.0
+    f = O.fwd(q, k, v, scale=0.5, causal=causal, bottom_right=bottom_right,
+              alibi_slopes=np.full(H, slope))
+    off = skv - sq if (bottom_right or not causal) else 0
+    for i in range(sq):
+        j = i + off
+        assert 0 <= j < skv
+        assert np.allclose(f["o"][0, :, i], v[0, :, j], atol=1e-12, rtol=0), i
+        s_diag = 0.5 * np.einsum("hd,hd->h", q[0, :, i], k[0, :, j])
+        assert np.allclose(f["lse"][0, :, i], s_diag, atol=1e-12, rtol=0), i
+
+
+def test_alibi_top_left_causal_is_a_per_key_bias():
+    # -slope (i - j) = slope j - slope i on the visible keys j <= i; the
+    # second term is constant along a row
+    B, H, S, D = 2, 2, 11, 6
+    q, k, v, dout = (_rand((B, H, S, D), 221 + i) for i in range(4))
+    slopes = np.array([[0.3, 1.1], [0.05, 0.7]])
+    a = O.bwd(q, k, v, dout, scale=0.45, causal=True, alibi_slopes=slopes)
+    key_bias = np.broadcast_to(slopes[:, :, None, None] * np.arange(S)[None, None, None, :],
+                               (B, H, S, S)).copy()
+    b = O.bwd(q, k, v, dout, scale=0.45, causal=True, bias=key_bias, want_dbias=False)
+    for name in ("o", "dq", "dk", "dv"):
+        assert np.allclose(a[name], b[name], atol=1e-12, rtol=1e-12), name
+    row_const = slopes[:, :, None] * np.arange(S)[None, None, :]
+    assert np.allclose(a["lse"], b["lse"] - row_const, atol=1e-12, rtol=0)
+
+
+def test_alibi_backward_central_differences():
+    B, H, Sq, Skv, Dq, Dv = 1, 2, 4, 6, 3, 4
+    q, k, v = _rand((B, H, Sq, Dq), 231), _rand((B, H, Skv, Dq), 232), _rand((B, H, Skv, Dv), 233)
+    dout = _rand((B, H, Sq, Dv), 234)
+    kw = dict(scale=0.6, alibi_slopes=np.array([[0.25, 0.9]]))
+    g = O.bwd(q, k, v, dout, **kw)
+    eps = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _loss(q, k, v, dout, None, **kw)
+            x[i] = old - eps
+            lm = _loss(q, k, v, dout, None, **kw)
+            x[i] = old
+            num[i] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(num - g[name])) / max(1e-3, np.max(np.abs(num)))
+        assert err < 1e-6, (name, err)
+
+
 # ------------------------------------------------------------ group mode ----
 def test_group_mode_equals_batch_mode_per_sequence():
     H, D = 2, 6
@@ -468,6 +541,10 @@ MUTANTS = {
     "rescale": ("double rescale = 1.0 / (1.0 - (double)h->p_drop);", "double rescale = 1.0;"),
     # a wrong Philox word order
     "philox": ("uint32_t n1 = lo1;", "uint32_t n1 = lo0;"),
+    # ALiBi with the wrong sign, without the absolute value, or misaligned
+    "alibi_sign": ("s[j] -= h->alibi_slope", "s[j] += h->alibi_slope"),
+    "alibi_abs": ("fabs((double)(j - i - h->alibi_off))", "((double)(j - i - h->alibi_off))"),
+    "alibi_off": ("(j - i - h->alibi_off)", "(j - i + h->alibi_off)"),
 }
 
 
