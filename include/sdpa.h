@@ -107,6 +107,17 @@ typedef struct {
      * gradient. */
     uint32_t mask_flags;
     int64_t window_left, window_right;
+    /* ALiBi position bias (Composable Kernel's FmhaBwdAlibiKargs: one fp32
+     * slope per batch entry and head, and the position encoding its backward
+     * kernel builds from the mask).  Nullable device pointer; when set,
+     *   s_ij += -alibi_slopes[b * alibi_batch_stride + h] * |j - i - off|
+     * with off = s_kv - s_q (per sequence) for a bottom-right mask or when
+     * there is no mask (is_causal = 0 and no SDPA_MASK_WINDOW), else 0.
+     * alibi_batch_stride = 0 shares one slope vector [h] across the batch.
+     * It takes the place of attn_bias: passing both is SDPA_ERR_UNSUPPORTED,
+     * and there is no gradient for the slopes. */
+    const float *alibi_slopes;
+    int64_t alibi_batch_stride;
 } sdpa_problem_t;
 
 #define SDPA_MASK_BOTTOM_RIGHT 1u

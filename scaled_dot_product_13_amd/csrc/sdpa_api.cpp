@@ -69,6 +69,8 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
                 (long long)p->h);
   if (p->mask_flags & ~(SDPA_MASK_BOTTOM_RIGHT | SDPA_MASK_WINDOW))
     return fail(SDPA_ERR_INVALID_ARG, "unknown mask_flags bits 0x%x", p->mask_flags);
+  if (p->alibi_slopes && p->alibi_batch_stride < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "alibi_batch_stride is negative");
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
   if (p->dtype == SDPA_F32) {
@@ -101,6 +103,17 @@ bool band_of(const sdpa_problem_t* p, int32_t& br, int32_t& lo, int32_t& hi) {
   hi = (int32_t)h;
   return l > -inf || h < inf;
 }
+// ALiBi alignment: the mask's, and bottom-right when there is no mask.
+int32_t alibi_bottom_right(const sdpa_problem_t* p) {
+  const bool masked = p->is_causal || (p->mask_flags & SDPA_MASK_WINDOW);
+  return (!masked || (p->mask_flags & SDPA_MASK_BOTTOM_RIGHT)) ? 1 : 0;
+}
+template <typename Args> void fill_alibi(const sdpa_problem_t* p, Args& a) {
+  a.alibi = p->alibi_slopes;
+  a.alibi_sb = p->alibi_batch_stride;
+  a.alibi_br = alibi_bottom_right(p);
+}
+
 bool banded(const sdpa_problem_t* p) {
   int32_t br, lo, hi;
   return band_of(p, br, lo, hi);
@@ -252,6 +265,8 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   if ((st = check_tensor(p, o, o_s, "o", vec)) != SDPA_OK) return st;
   const bool group = p->cu_seqlens_q != nullptr;
   if (attn_bias) {
+    if (p->alibi_slopes)
+      return fail(SDPA_ERR_UNSUPPORTED, "attn_bias and alibi_slopes cannot be combined");
     if (group) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
     if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
   }
@@ -267,6 +282,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.bias_vec = bias_vec_ok(p, attn_bias, bias_s) ? 1 : 0;
   a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
   band_of(p, a.band_br, a.band_lo, a.band_hi);
+  fill_alibi(p, a);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
@@ -277,7 +293,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
                  (long long)p->s_q, (long long)p->s_kv, (long long)p->d_qk, (long long)p->d_v,
                  p->is_causal, attn_bias != nullptr, (double)p->dropout_probability, group);
   hipError_t e;
-  if (decode_eligible(p, attn_bias != nullptr)) {
+  if (decode_eligible(p, attn_bias != nullptr || p->alibi_slopes != nullptr)) {
     // thin query: split-KV when the workspace holds the partials, else one
     // split per (batch, key/value head, row group)
     sdpa::DecodePlan pl = decode_plan(p);
@@ -311,6 +327,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
 static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
   a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
   band_of(p, a.band_br, a.band_lo, a.band_hi);
+  fill_alibi(p, a);
   a.seq = seq_info(p);
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
@@ -366,6 +383,8 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   if (!softmax_lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null (the backward needs the stats)");
   const bool group = p->cu_seqlens_q != nullptr;
   if (attn_bias) {
+    if (p->alibi_slopes)
+      return fail(SDPA_ERR_UNSUPPORTED, "attn_bias and alibi_slopes cannot be combined");
     if (group) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
     if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
   }
@@ -429,6 +448,8 @@ static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sd
   if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
   if (!stats) return fail(SDPA_ERR_INVALID_ARG, "stats is null (run sdpa_bwd_preprocess first)");
   if (attn_bias) {
+    if (p->alibi_slopes)
+      return fail(SDPA_ERR_UNSUPPORTED, "attn_bias and alibi_slopes cannot be combined");
     if (p->cu_seqlens_q) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
     if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
   }

@@ -133,6 +133,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     return (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
   };
   const bool want_dbias = BIAS && a.dbias != nullptr;
+  const bool alibi = BIAS && a.alibi != nullptr;  // computed in place of the bias tensor
 
   const int wk0 = kv0 + 32 * kb;  // this wave's first key
   const int kvr = wk0 + l32;      // this lane's key
@@ -244,6 +245,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     const int q0 = it.q0, h = it.h;
     const uint32_t bh = (uint32_t)(b * a.H + h);
     const uint16_t* bg = BIAS ? bias_head(h) : nullptr;
+    const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sq, skv);
     const auto vQ = rdQ.view(sQ[set]);
     const auto vOt = rdOt.view(sO[set]);
     // Operand reads issue in source order (their address XORs are volatile),
@@ -293,7 +295,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         if (BIAS) {
           const int ql = lb + e, qr = q0 + ql;
           float bval = 0.f;
-          if (bias_lds)
+          if (alibi)
+            bval = alibi_at(at, kvr, qr);
+          else if (bias_lds)
             bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * kb + l32)));
           else if (kv_ok && qr < sq)
             bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
@@ -528,6 +532,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   const T* dog = base_ptr<T>(a.dout, a.sdo_, sp, h, true);
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+  const bool alibi = BIAS && a.alibi != nullptr;  // computed in place of the bias tensor
+  const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sq, skv);
 
   // banded: the tile's rows see only keys [q0 + lo, r_last + hi]
   const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
@@ -615,7 +621,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     const bool active = !BAND || (n0 - (wq0 + 31) <= bd.hi && n0 + BC - 1 - wq0 >= bd.lo);
 
     uint32_t braw[4][4];
-    if (BIAS && active) {
+    if (BIAS && active && !alibi) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         int kb = n0 + 16 * u + 8 * g;
@@ -664,20 +670,32 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     // have Q = dO = 0 and LSE = D = 0, so their dS is exactly 0 without a
     // mask; keys past s_kv or outside the band are zeroed on the tiles
     // that have them.
+    if (BIAS && alibi) {
+      keep_branch();
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x;
-        if (BIAS) {
-          const int u = 2 * blk + (r >> 3), e = r & 7;
-          const uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          x = __builtin_fmaf(s[blk][r], c, __builtin_fmaf(to_f32<T>((uint16_t)bits), kLog2e, -lse2));
-        } else {
-          x = __builtin_fmaf(s[blk][r], c, -lse2);
+        for (int r = 0; r < 16; ++r) {
+          const int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+          const float x = __builtin_fmaf(s[blk][r], c, __builtin_fmaf(alibi_at(at, kv, row), kLog2e, -lse2));
+          s[blk][r] = __builtin_amdgcn_exp2f(x);
         }
-        s[blk][r] = __builtin_amdgcn_exp2f(x);
-      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x;
+          if (BIAS) {
+            const int u = 2 * blk + (r >> 3), e = r & 7;
+            const uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            x = __builtin_fmaf(s[blk][r], c, __builtin_fmaf(to_f32<T>((uint16_t)bits), kLog2e, -lse2));
+          } else {
+            x = __builtin_fmaf(s[blk][r], c, -lse2);
+          }
+          s[blk][r] = __builtin_amdgcn_exp2f(x);
+        }
+    }
     const bool need_mask =
         (n0 + BC > skv) || (BAND && !(n0 - (wq0 + 31) >= bd.lo && n0 + BC - 1 - wq0 <= bd.hi));
     if (need_mask) {
@@ -752,9 +770,10 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
   const float* doi = base_ptr<float>(a.dout, a.sdo_, sp, h, true) + (int64_t)i * a.sdo_.s;
   const float* kg = base_ptr<float>(a.k, a.sk_, sp, h / a.G, false);
   const float* vg = base_ptr<float>(a.v, a.sv_, sp, h / a.G, false);
-  const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
-                                 (int64_t)i * a.sb_.s
-                           : nullptr;
+  const float* brow = (BIAS && a.bias) ? (const float*)a.bias + (int64_t)b * a.sb_.b +
+                                            (int64_t)h * a.sb_.h + (int64_t)i * a.sb_.s
+                                      : nullptr;
+  const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sp.sq, sp.skv);
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
   const uint32_t bh = (uint32_t)(b * a.H + h);
@@ -785,7 +804,7 @@ __global__ void __launch_bounds__(256) dq_f32(const BwdArgs a, int dqk, int dv) 
       if (d < dqk) ps += q[c] * kj[d];
       if (d < dv) pd += dO[c] * vj[d];
     }
-    float s = wave_sum(ps) * a.scale + (BIAS ? brow[j] : 0.f);
+    float s = wave_sum(ps) * a.scale + (BIAS ? (brow ? brow[j] : alibi_at(at, j, i)) : 0.f);
     float dp = wave_sum(pd);
     float p = exp2f(s * kLog2e - lse2);
     float z = 1.f;
@@ -836,8 +855,10 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
   for (int h = hk * a.G; h < (hk + 1) * a.G; ++h) {
     const float* qg = base_ptr<float>(a.q, a.sq_, sp, h, true);
     const float* dog = base_ptr<float>(a.dout, a.sdo_, sp, h, true);
-    const float* bcol =
-        BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h + j : nullptr;
+    const float* bcol = (BIAS && a.bias)
+                            ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h + j
+                            : nullptr;
+    const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sp.sq, sp.skv);
     float* dbcol = (BIAS && a.dbias)
                        ? (float*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h + j
                        : nullptr;
@@ -857,7 +878,8 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
         if (d < dqk) ps += qi[d] * k[c];
         if (d < dv) pd += doi[d] * v[c];
       }
-      float s = wave_sum(ps) * a.scale + (BIAS ? bcol[(int64_t)i * a.sb_.s] : 0.f);
+      float s = wave_sum(ps) * a.scale +
+                (BIAS ? (bcol ? bcol[(int64_t)i * a.sb_.s] : alibi_at(at, j, i)) : 0.f);
       float dp = wave_sum(pd);
       float p = exp2f(s * kLog2e - a.lse2[d_base + i]);
       float z = 1.f;
@@ -942,7 +964,7 @@ static hipError_t dq_type(int dqk, int dv, bool causal, bool bias, bool drop, bo
 }
 
 hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st) {
-  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  const bool bias = a.bias != nullptr || a.alibi != nullptr, drop = a.drop.enabled != 0;
   if (t == IoType::BF16) return dkdv_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
   if (t == IoType::F16) return dkdv_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
   dim3 grid((a.seq.s_kv + 3) / 4, a.H / a.G, a.B), block(256);
@@ -954,7 +976,7 @@ hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs
 
 hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& a, hipStream_t st,
                          bool with_pre) {
-  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  const bool bias = a.bias != nullptr || a.alibi != nullptr, drop = a.drop.enabled != 0;
   if (t == IoType::BF16) return dq_type<__bf16>(dqk, dv, causal, bias, drop, with_pre, a, st);
   if (t == IoType::F16) return dq_type<_Float16>(dqk, dv, causal, bias, drop, with_pre, a, st);
   if (with_pre) return hipErrorInvalidValue;  // the fp32 path keeps the separate preprocess

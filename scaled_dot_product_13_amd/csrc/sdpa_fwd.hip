@@ -64,6 +64,9 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   T* og = base_ptr_mut<T>(a.o, a.so_, sp, h, true);
   const uint16_t* bg = nullptr;
   if (BIAS) bg = (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+  // ALiBi takes the bias path's place (computed, not loaded)
+  const bool alibi = BIAS && a.alibi != nullptr;
+  const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sp.sq, sp.skv);
 
   // keys visible from some row of this tile: [k_begin, k_end), in key
   // tiles t0 .. t0 + nt - 1
@@ -138,7 +141,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     // bias for this lane's row: runs of 8 consecutive keys (issued before
     // the next tile's prefetch so that waiting for them does not wait for it)
     uint32_t braw[2 * NBLK][4];
-    if (BIAS && active) {
+    if (BIAS && active && !alibi) {
 #pragma unroll
       for (int u = 0; u < 2 * NBLK; ++u) {
         int kb = n0 + 16 * u + 8 * g;  // u = 2*blk + hh
@@ -191,14 +194,25 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
     };
     float mrow;
     if (BIAS) {
+      if (alibi) {
+        keep_branch();
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk)
+        for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int u = 2 * blk + (r >> 3), e = r & 7;
-          uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          s[blk][r] = __builtin_fmaf(s[blk][r], c, to_f32<T>((uint16_t)bits) * kLog2e);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
+            s[blk][r] = __builtin_fmaf(s[blk][r], c, alibi_at(at, kv, row) * kLog2e);
+          }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int u = 2 * blk + (r >> 3), e = r & 7;
+            uint32_t bits = (braw[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            s[blk][r] = __builtin_fmaf(s[blk][r], c, to_f32<T>((uint16_t)bits) * kLog2e);
+          }
+      }
       if (need_mask) {
         keep_branch();
 #pragma unroll
@@ -343,9 +357,10 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
   const float* kg = base_ptr<float>(a.k, a.sk_, sp, h / a.G, false);
   const float* vg = base_ptr<float>(a.v, a.sv_, sp, h / a.G, false);
   float* og = base_ptr_mut<float>(a.o, a.so_, sp, h, true) + (int64_t)row * a.so_.s;
-  const float* brow = BIAS ? (const float*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h +
-                                 (int64_t)row * a.sb_.s
-                           : nullptr;
+  const float* brow = (BIAS && a.bias) ? (const float*)a.bias + (int64_t)b * a.sb_.b +
+                                            (int64_t)h * a.sb_.h + (int64_t)row * a.sb_.s
+                                      : nullptr;
+  const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sp.sq, sp.skv);
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
   const uint32_t bh = (uint32_t)(b * a.H + h);
@@ -371,7 +386,7 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
       int d = lane + 64 * c;
       if (d < dqk) part += q[c] * kj[d];
     }
-    float sc = wave_sum(part) * a.scale + (BIAS ? brow[j] : 0.f);
+    float sc = wave_sum(part) * a.scale + (BIAS ? (brow ? brow[j] : alibi_at(at, j, row)) : 0.f);
     float mn = fmaxf(m, sc);
     float alpha = expf(m - mn);
     float p = expf(sc - mn);
@@ -440,7 +455,7 @@ bool mfma_dims_supported(int dqk, int dv) {
 }
 
 hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a, hipStream_t st) {
-  const bool bias = a.bias != nullptr, drop = a.drop.enabled != 0;
+  const bool bias = a.bias != nullptr || a.alibi != nullptr, drop = a.drop.enabled != 0;
   if (t == IoType::BF16) return fwd_dispatch_dims<__bf16>(dqk, dv, causal, bias, drop, a, st);
   if (t == IoType::F16) return fwd_dispatch_dims<_Float16>(dqk, dv, causal, bias, drop, a, st);
   dim3 grid((a.seq.s_q + 3) / 4, a.H, a.B), block(256);

@@ -101,6 +101,23 @@ __device__ __forceinline__ Band seq_band(int32_t br, int32_t lo, int32_t hi, int
   return b;
 }
 
+// ALiBi of one (sequence, head): the term is slope * |j - i - off|
+// (slope already negated), zero slope when there is none.
+struct AlibiTerm {
+  float slope;
+  int32_t off;
+};
+__device__ __forceinline__ AlibiTerm alibi_term(const float* alibi, int64_t sb, int32_t br, int b,
+                                                int h, int sq, int skv) {
+  AlibiTerm t;
+  t.slope = alibi ? -alibi[(int64_t)b * sb + h] : 0.f;
+  t.off = br ? skv - sq : 0;
+  return t;
+}
+__device__ __forceinline__ float alibi_at(const AlibiTerm& t, int kv, int row) {
+  return t.slope * fabsf((float)(kv - row - t.off));
+}
+
 struct DropKey {
   uint32_t k0, k1, off, thr;
 };

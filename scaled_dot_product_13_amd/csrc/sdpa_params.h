@@ -45,6 +45,12 @@ struct FwdArgs {
   // band mask: key j visible from row i iff lo <= j - i - off <= hi, with
   // off = s_kv - s_q (per sequence) when band_br, else 0; +-kBandInf = unbounded
   int32_t band_br, band_lo, band_hi;
+  // ALiBi (nullable; then the BIAS kernels take it in place of the bias
+  // tensor): s_ij += -alibi[b * alibi_sb + h] * |j - i - off|, off = s_kv -
+  // s_q (per sequence) when alibi_br, else 0
+  const float* alibi;
+  int64_t alibi_sb;
+  int32_t alibi_br;
   SeqInfo seq;
   float scale;         // scaling_factor
   float scale_log2;    // scaling_factor * log2(e)
@@ -66,6 +72,10 @@ struct BwdArgs {
   // band mask: key j visible from row i iff lo <= j - i - off <= hi, with
   // off = s_kv - s_q (per sequence) when band_br, else 0; +-kBandInf = unbounded
   int32_t band_br, band_lo, band_hi;
+  // ALiBi, as in FwdArgs
+  const float* alibi;
+  int64_t alibi_sb;
+  int32_t alibi_br;
   SeqInfo seq;
   float scale, scale_log2;
   DropoutArgs drop;

@@ -47,6 +47,7 @@ class Problem(ctypes.Structure):
         ("h_kv", ctypes.c_int64),
         ("mask_flags", ctypes.c_uint32), ("window_left", ctypes.c_int64),
         ("window_right", ctypes.c_int64),
+        ("alibi_slopes", ctypes.c_void_p), ("alibi_batch_stride", ctypes.c_int64),
     ]
 
 
@@ -134,13 +135,18 @@ def _stream():
 
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
-                 max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None):
+                 max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None,
+                 alibi_slopes=None):
     """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group
     [T,H,D]); k and v may have fewer heads than q (grouped-query attention).
 
     Mask: row i sees key j iff -window_left <= j - i - off <= window_right
     (a window side that is None is unbounded; causal caps window_right at 0),
-    off = s_kv - s_q per sequence with bottom_right, else 0."""
+    off = s_kv - s_q per sequence with bottom_right, else 0.
+
+    alibi_slopes: fp32 device tensor [B, H] (or [H], shared by the batch);
+    adds -slope |j - i - off'| to the scores, off' the mask's alignment
+    (bottom-right without a mask).  The tensor must outlive the call."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     group = cu_seqlens_q is not None
@@ -165,6 +171,11 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     p.mask_flags = (MASK_BOTTOM_RIGHT if bottom_right else 0) | (MASK_WINDOW if windowed else 0)
     p.window_left = -1 if window_left is None else int(window_left)
     p.window_right = -1 if window_right is None else int(window_right)
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.stride(-1) != 1:
+            raise TypeError("alibi_slopes must be a float32 tensor with unit stride along heads")
+        p.alibi_slopes = alibi_slopes.data_ptr()
+        p.alibi_batch_stride = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     p.dropout_probability = float(dropout_p)
     p.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     p.dropout_offset = int(offset) & 0xFFFFFFFFFFFFFFFF
@@ -176,7 +187,7 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
              seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
              max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None,
              bottom_right=False, window_left=None, window_right=None, split_kv=True,
-             workspace=None):
+             workspace=None, alibi_slopes=None):
     """Forward.  Returns (o, lse or None, keep or None).  split_kv=False
     passes no workspace, so a thin-query problem runs unsplit; `workspace`
     (uint8, at least fwd_workspace_size bytes) avoids an allocation."""
@@ -185,7 +196,8 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
                      offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
                      max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
-                     window_left=window_left, window_right=window_right)
+                     window_left=window_left, window_right=window_right,
+                     alibi_slopes=alibi_slopes)
     if out is None:
         oshape = list(q.shape)
         oshape[-1] = v.shape[-1]
@@ -211,14 +223,15 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
 def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, dropout_p=0.0,
              seed=0, offset=0, seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None,
              max_seqlen_q=None, max_seqlen_kv=None, want_dbias=False, workspace=None,
-             bottom_right=False, window_left=None, window_right=None):
+             bottom_right=False, window_left=None, window_right=None, alibi_slopes=None):
     """Backward.  Returns (dq, dk, dv, dbias or None)."""
     group = cu_seqlens_q is not None
     p = make_problem(q, k, v, scale=scale, causal=causal, dropout_p=dropout_p, seed=seed,
                      offset=offset, seed_offset=seed_offset, cu_seqlens_q=cu_seqlens_q,
                      cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
                      max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
-                     window_left=window_left, window_right=window_right)
+                     window_left=window_left, window_right=window_right,
+                     alibi_slopes=alibi_slopes)
     if dout.stride(-1) != 1:
         dout = dout.contiguous()
     dq, dk, dv = _alloc_like(q, q.shape), _alloc_like(k, k.shape), _alloc_like(v, v.shape)

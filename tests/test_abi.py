@@ -56,6 +56,8 @@ def _problem(S, **kw):
     p.h_kv = kw.get("hkv", 0)
     p.mask_flags = kw.get("mask_flags", 0)
     p.window_left, p.window_right = kw.get("window", (-1, -1))
+    if "alibi" in kw:
+        p.alibi_slopes, p.alibi_batch_stride = kw["alibi"]
     return p
 
 
@@ -107,6 +109,13 @@ def test_invalid_arguments(S):
     assert _fwd(S, _problem(S, mask_flags=4)) == S.SDPA_ERR_INVALID_ARG
     assert b"mask_flags" in L.sdpa_last_error_message()
     assert _bwd(S, _problem(S, mask_flags=0x80000000)) == S.SDPA_ERR_INVALID_ARG
+    # ALiBi: a negative batch stride is invalid; it cannot be combined with a
+    # bias tensor
+    assert _fwd(S, _problem(S, alibi=(FAKE, -1))) == S.SDPA_ERR_INVALID_ARG
+    assert b"alibi_batch_stride" in L.sdpa_last_error_message()
+    assert _fwd(S, _problem(S, alibi=(FAKE, 2)), bias=FAKE) == S.SDPA_ERR_UNSUPPORTED
+    assert b"alibi_slopes" in L.sdpa_last_error_message()
+    assert _bwd(S, _problem(S, alibi=(FAKE, 0)), bias=FAKE) == S.SDPA_ERR_UNSUPPORTED
 
 
 def test_problem_struct_matches_the_header(S):

@@ -97,7 +97,7 @@ def _mask_kw(wl):
 
 
 def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd",
-                 kv_lengths=None, fwd_kw=None):
+                 kv_lengths=None, fwd_kw=None, alibi=None):
     """Run fwd+bwd on the GPU and compare with the oracle on `heads`
     (all heads when None).  Returns the max errors."""
     x = inputs.make_inputs(wl, lengths, kv_lengths)
@@ -115,6 +115,8 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
     if group:
         kw.update(cu_seqlens_q=x["cu_seqlens"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
                   max_seqlen_q=x["max_seqlen"], max_seqlen_kv=x["max_seqlen_kv"])
+    if alibi is not None:
+        kw["alibi_slopes"] = alibi.to(dev)
     want_keep = check_keep and wl.dropout_p > 0 and not group
     _say(wl.name, wl.dtype, "B", wl.b, "H", wl.h, "Sq", wl.s_q, "Skv", wl.s_kv, "d", wl.d_qk,
          wl.d_v, "causal", wl.causal, "bias", wl.bias, "p", wl.dropout_p, "group", group, layout,
@@ -128,6 +130,8 @@ def run_workload(S, wl, heads=None, lengths=None, check_keep=True, layout="bhsd"
     if group:
         okw.update(cu_seqlens_q=x["cu_seqlens"].numpy().astype(np.int64),
                    cu_seqlens_kv=x["cu_seqlens_kv"].numpy().astype(np.int64))
+    if alibi is not None:
+        okw["alibi_slopes"] = alibi.double().numpy()
     f64 = lambda t: t.double().numpy() if t is not None else None
     ref = O.bwd(f64(q), f64(k), f64(v), f64(dout), bias=f64(bias), heads=heads, **okw)
     rkeep = None
@@ -326,6 +330,44 @@ def test_decode_workload_full(S):
         _cmp("o", _np(got_o), ref["o"], x["dtype"])
         _cmp("lse", _np(got_lse), ref["lse"], x["dtype"])
     _say("max |o - ref|", float(np.max(np.abs(_np(o) - ref["o"]))))
+
+
+def _alibi_slopes(n_batch, n_heads, seed, shared=False):
+    """ALiBi slopes: the usual geometric sequence 2^(-8 k / H), k = 1..H,
+    jittered per batch entry (or shared by the batch: shape [H])."""
+    base = torch.tensor([2.0 ** (-8.0 * (k + 1) / n_heads) for k in range(n_heads)])
+    if shared:
+        return base.float()
+    g = torch.Generator().manual_seed(seed)
+    return (base[None, :] * (0.5 + torch.rand((n_batch, n_heads), generator=g))).float()
+
+
+ALIBI = [
+    # dtype, dims, s_q, s_kv, causal, p, bottom_right, window_left, h, h_kv, shared
+    ("bf16", (128, 128), 300, 300, True, 0.0, False, None, 2, 2, False),
+    ("f16", (64, 64), 200, 330, False, 0.0, False, None, 2, 2, False),  # bottom-right (no mask)
+    ("bf16", (192, 128), 150, 400, True, 0.1, True, None, 2, 2, False),
+    ("bf16", (128, 128), 260, 260, True, 0.0, False, 64, 2, 2, True),  # top-left window
+    ("f16", (128, 128), 190, 190, False, 0.0, False, None, 4, 2, True),  # grouped-query
+    ("bf16", (128, 128), 1, 500, False, 0.0, False, None, 8, 2, False),  # thin query, main forward
+    ("f32", (64, 64), 90, 120, True, 0.1, True, None, 2, 2, False),
+    ("f32", (64, 64), 70, 70, False, 0.0, False, None, 2, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", ALIBI, ids=lambda c: f"{c[0]}-d{c[1][0]}-{c[2]}x{c[3]}-c{int(c[4])}"
+                         f"-p{c[5]}-br{int(c[6])}-w{c[7]}-h{c[8]}kv{c[9]}-sh{int(c[10])}")
+def test_alibi_parity(S, case):
+    dt, (dq_, dv_), sq, skv, causal, p, br, wl_, h, hkv, shared = case
+    wl = inputs.small(dt, b=2, h=h, h_kv=hkv, s_q=sq, s_kv=skv, d_qk=dq_, d_v=dv_, causal=causal,
+                      dropout_p=p, seed=sq + 5 * skv, bottom_right=br, window_left=wl_)
+    run_workload(S, wl, alibi=_alibi_slopes(2, h, sq, shared))
+
+
+def test_alibi_varlen(S):
+    lengths, kv_lengths = [90, 1, 200], [150, 40, 200]
+    wl = inputs.small("bf16", b=3, h=4, h_kv=2, d_qk=128, d_v=128, seed=37, varlen=(3, 1, 200))
+    run_workload(S, wl, lengths=lengths, kv_lengths=kv_lengths, alibi=_alibi_slopes(3, 4, 37))
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
