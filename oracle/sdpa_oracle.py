@@ -215,6 +215,22 @@ def _alibi(alibi_slopes, n_batch, n_heads, causal, bottom_right, window_left, wi
     return sl, (bottom_right or not masked)
 
 
+def dequantize_kv(codes, scales, group_size, zero_points=None):
+    """K or V from 8-bit integer codes with one scale (and optionally one
+    integer zero point) per token and per group of `group_size` consecutive
+    head-dim elements: x_c = (code_c - zp_{c // g}) * scale_{c // g}.  This is
+    the grouped key / value quantization of the oneDNN micro SDPA host driver
+    (key scales grouped along the head dimension per key, value scales
+    grouped along the head dimension per value row, zero points subtracted
+    before scaling).  codes [..., D]; scales, zero_points [..., D / g]."""
+    x = np.asarray(codes, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % group_size == 0 and scales.shape[-1] == d // group_size
+    if zero_points is not None:
+        x = x - np.repeat(np.asarray(zero_points, dtype=np.float64), group_size, axis=-1)
+    return x * np.repeat(np.asarray(scales, dtype=np.float64), group_size, axis=-1)
+
+
 def _run(fn, heads, threads):
     arr = (_Head * len(heads))(*heads)
     getattr(lib(), fn)(arr, len(heads), int(threads))

@@ -11,6 +11,9 @@ Every test here runs on the CPU.  What pins what:
     oracle's own forward, torch float64 autograd of the forward, and
     invariants (row sums of dS vanish, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
   - group mode: equals batch mode run sequence by sequence.
+  - quantized K/V: per-group symmetric int8 quantization of real data
+    dequantizes to within half a step (the rounding bound); shifting codes
+    and zero points together changes nothing; unit scales are the identity.
   - ALiBi: slope 0 is the plain forward; a very steep slope leaves only the
     key on the aligned diagonal (O_i = V_{i+off}); under a top-left causal
     mask it equals a per-key bias slope * j (the -slope * i part is constant
@@ -496,6 +499,39 @@ def test_alibi_backward_central_differences():
             num[i] = (lp - lm) / (2 * eps)
         err = np.max(np.abs(num - g[name])) / max(1e-3, np.max(np.abs(num)))
         assert err < 1e-6, (name, err)
+
+
+# --------------------------------------------------------- quantized K/V ----
+@pytest.mark.parametrize("group", [16, 32, 128])
+def test_dequantize_is_within_half_a_step_of_the_quantized_data(group):
+    # a test-side symmetric quantizer: scale = max|x| / 127 per token and
+    # group, code = round(x / scale); dequantizing must land within scale / 2
+    x = _rand((2, 3, 40, 128), 241)
+    xg = x.reshape(2, 3, 40, 128 // group, group)
+    scale = np.abs(xg).max(-1) / 127.0
+    codes = np.clip(np.rint(xg / scale[..., None]), -127, 127).astype(np.int8).reshape(x.shape)
+    xr = O.dequantize_kv(codes, scale, group)
+    bound = np.repeat(scale, group, axis=-1) / 2
+    assert np.all(np.abs(xr - x) <= bound * (1 + 1e-12))
+    # and the quantization is not trivially coarse: errors use the whole step
+    assert np.max(np.abs(xr - x) / bound) > 0.9
+
+
+def test_dequantize_zero_point_shift_and_identity():
+    rng = np.random.default_rng(251)
+    codes = rng.integers(-100, 100, size=(4, 7, 64)).astype(np.int8)
+    zp = rng.integers(-20, 20, size=(4, 7, 4)).astype(np.int8)
+    sc = rng.uniform(0.01, 0.2, size=(4, 7, 4))
+    a = O.dequantize_kv(codes, sc, 16, zp)
+    c = 7
+    b = O.dequantize_kv((codes.astype(np.int16) + c), sc, 16, zp.astype(np.int16) + c)
+    assert np.array_equal(a, b)
+    assert np.array_equal(O.dequantize_kv(codes, np.ones((4, 7, 1)), 64), codes.astype(np.float64))
+    # one group per 16 columns: column c uses group c // 16
+    one = np.zeros((1, 1, 64), dtype=np.int8)
+    one[0, 0, 17] = 1
+    g = np.array([[[1.0, 3.0, 5.0, 7.0]]])
+    assert O.dequantize_kv(one, g, 16)[0, 0, 17] == 3.0
 
 
 # ------------------------------------------------------------ group mode ----
