@@ -14,7 +14,9 @@ The line also carries a "decode" object: the thin-query forward (split-KV)
 on the decode workload (bf16, B=16, 32 query heads over 8 key/value heads,
 one query row per sequence, S_kv=8192, d=128), timed the same way and
 reported as algorithmic HBM bytes (K, V, Q, O, LSE) per second against the
-8 TB/s peak.
+8 TB/s peak; and "decode_int8": the same step over an int8 K/V cache with
+fp32 scales per token and group of 32 head-dim elements (bytes: codes,
+scales, Q, O, LSE).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
@@ -88,17 +90,25 @@ def cpu_baseline(wl, x, budget_heads):
                       f"same workload, fp64, {dt:.1f} s wall"}
 
 
-def decode_bench(S, torch, steps, warmup):
-    """Time the thin-query forward on the decode workload: HIP events on the
+def decode_bench(S, torch, steps, warmup, wl):
+    """Time the thin-query forward on a decode workload: HIP events on the
     launch stream around each sdpa_fwd call (the split kernel and, when the
     keys are split, the combine kernel)."""
     from scaled_dot_product_13_amd import inputs
-    wl = inputs.DECODE
     x = inputs.make_inputs(wl)
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
-    del x
     kw = dict(scale=wl.softmax_scale, causal=wl.causal, bottom_right=wl.bottom_right)
+    hk = wl.h_kv or wl.h
+    kv_elems = wl.b * hk * wl.s_kv * (wl.d_qk + wl.d_v)
+    if wl.kv_quant is not None:
+        gs, with_zp = wl.kv_quant
+        kw.update(kv_scales=(x["k_scales"].to(dev), x["v_scales"].to(dev)), kv_group_size=gs,
+                  kv_zero_points=(x["k_zp"].to(dev), x["v_zp"].to(dev)) if with_zp else None)
+        kv_bytes = kv_elems + kv_elems // gs * (4 + (1 if with_zp else 0))
+    else:
+        kv_bytes = 2 * kv_elems
+    del x
     o = torch.empty((wl.b, wl.h, wl.s_q, wl.d_v), dtype=q.dtype, device=dev)
     lse = torch.empty((wl.b, wl.h, wl.s_q), dtype=torch.float32, device=dev)
     ws = torch.empty(max(S.fwd_workspace_size(q, k, v, **kw), 1), dtype=torch.uint8, device=dev)
@@ -115,10 +125,8 @@ def decode_bench(S, torch, steps, warmup):
         ev.append((e0, e1))
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    hk = wl.h_kv or wl.h
-    es = 2  # bf16
-    byts = (es * wl.b * hk * wl.s_kv * (wl.d_qk + wl.d_v)        # K, V
-            + es * wl.b * wl.h * wl.s_q * (wl.d_qk + wl.d_v)     # Q, O
+    byts = (kv_bytes                                             # K, V (+ scales)
+            + 2 * wl.b * wl.h * wl.s_q * (wl.d_qk + wl.d_v)      # Q, O (bf16)
             + 4 * wl.b * wl.h * wl.s_q)                          # LSE
     gbs = byts / (ms * 1e-3) / 1e9
     return {"workload": wl.name, "ms": round(ms, 5), "bytes": byts,
@@ -239,7 +247,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_decode:
-        out["decode"] = decode_bench(S, torch, args.steps, args.warmup)
+        out["decode"] = decode_bench(S, torch, args.steps, args.warmup, inputs.DECODE)
+        out["decode_int8"] = decode_bench(S, torch, args.steps, args.warmup, inputs.DECODE_Q8)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_heads)
     else:

@@ -71,6 +71,8 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
     return fail(SDPA_ERR_INVALID_ARG, "unknown mask_flags bits 0x%x", p->mask_flags);
   if (p->alibi_slopes && p->alibi_batch_stride < 0)
     return fail(SDPA_ERR_INVALID_ARG, "alibi_batch_stride is negative");
+  if (p->kv_quant != SDPA_KV_QUANT_NONE && p->kv_quant != SDPA_KV_QUANT_S8)
+    return fail(SDPA_ERR_INVALID_ARG, "unknown kv_quant %d", p->kv_quant);
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
   if (p->dtype == SDPA_F32) {
@@ -206,6 +208,36 @@ int64_t decode_target_wgs() {
   }();
   return n;
 }
+// int8 K/V: everything the thin-query kernel's int8 mode assumes.
+sdpa_status_t check_kv_quant(const sdpa_problem_t* p, bool has_bias, const void* k,
+                             sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s) {
+  if (p->dtype == SDPA_F32 || has_bias || p->dropout_probability > 0.f || p->s_q > sdpa::kDecodeMaxSq)
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs a thin-query forward: 16-bit q, s_q <= %lld, "
+                "no bias, ALiBi or dropout", (long long)sdpa::kDecodeMaxSq);
+  if (!decode_eligible(p, false))
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs the thin-query kernel (SDPA_DECODE=0 is set)");
+  if (p->d_qk != 128 || p->d_v != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs d_qk = d_v = 128");
+  const int g = p->kv_group_size;
+  if (!(g == 16 || g == 32 || g == 64 || g == 128))
+    return fail(SDPA_ERR_UNSUPPORTED, "kv_group_size %d not in {16, 32, 64, 128}", g);
+  if (!p->k_scales || !p->v_scales) return fail(SDPA_ERR_INVALID_ARG, "k_scales / v_scales are null");
+  if ((p->k_zero_points == nullptr) != (p->v_zero_points == nullptr))
+    return fail(SDPA_ERR_INVALID_ARG, "k_zero_points and v_zero_points must both be set or both null");
+  const sdpa_strides_t ss = p->kv_scale_strides;
+  if (ss.batch < 0 || ss.head < 0 || ss.seq < 0)
+    return fail(SDPA_ERR_INVALID_ARG, "kv_scale_strides has a negative stride");
+  const bool group = p->cu_seqlens_q != nullptr;
+  for (int i = 0; i < 2; ++i) {
+    const void* t = i ? v : k;
+    const sdpa_strides_t s = i ? v_s : k_s;
+    if ((uintptr_t)t % 16 || s.head % 16 || s.seq % 16 || (!group && s.batch % 16))
+      return fail(SDPA_ERR_UNSUPPORTED, "int8 %s: base and strides must be multiples of 16 bytes",
+                  i ? "v" : "k");
+  }
+  return SDPA_OK;
+}
+
 sdpa::DecodePlan decode_plan(const sdpa_problem_t* p) {
   return sdpa::plan_decode(p->b, p->h, kv_group(p), p->s_q, p->s_kv, decode_target_wgs());
 }
@@ -260,8 +292,9 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   if (empty_problem(p)) return SDPA_OK;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
-  if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;
-  if ((st = check_tensor(p, v, v_s, "v", vec)) != SDPA_OK) return st;
+  const bool q8 = p->kv_quant == SDPA_KV_QUANT_S8;
+  if ((st = check_tensor(p, k, k_s, "k", vec && !q8)) != SDPA_OK) return st;
+  if ((st = check_tensor(p, v, v_s, "v", vec && !q8)) != SDPA_OK) return st;
   if ((st = check_tensor(p, o, o_s, "o", vec)) != SDPA_OK) return st;
   const bool group = p->cu_seqlens_q != nullptr;
   if (attn_bias) {
@@ -270,6 +303,8 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
     if (group) return fail(SDPA_ERR_UNSUPPORTED, "attn_bias is not supported in group (varlen) mode");
     if ((st = check_tensor(p, attn_bias, bias_s, "attn_bias", false)) != SDPA_OK) return st;
   }
+  if (q8 && (st = check_kv_quant(p, attn_bias || p->alibi_slopes, k, k_s, v, v_s)) != SDPA_OK)
+    return st;
   if (dropout_keep_out && group)
     return fail(SDPA_ERR_UNSUPPORTED, "dropout_keep_out is only available in batch mode");
 
@@ -303,6 +338,14 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
       pl.ns = 1;
     }
     sdpa::DecodeArgs d{};
+    if (q8) {
+      d.k_sc = p->k_scales;
+      d.v_sc = p->v_scales;
+      d.k_zp = p->k_zero_points;
+      d.v_zp = p->v_zero_points;
+      d.ss = to_str(p->kv_scale_strides);
+      d.qgs = p->kv_group_size;
+    }
     d.ns = pl.ns;
     d.chunk = pl.chunk;
     d.rg = pl.rg;
@@ -341,6 +384,8 @@ sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t* p, const void* o, sdpa_s
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
+  if (p->kv_quant != SDPA_KV_QUANT_NONE)
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
   if (empty_problem(p)) return SDPA_OK;
   if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
   if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
@@ -370,6 +415,8 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   g_msg[0] = 0;
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
+  if (p->kv_quant != SDPA_KV_QUANT_NONE)
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
   if (empty_problem(p)) return SDPA_OK;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
@@ -441,6 +488,8 @@ static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sd
                                       sdpa_strides_t bias_s, const void* d_o, sdpa_strides_t do_s,
                                       const float* stats) {
   sdpa_status_t st;
+  if (p->kv_quant != SDPA_KV_QUANT_NONE)
+    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
   if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;

@@ -511,8 +511,13 @@ template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP, bool PRE
 __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(const BwdArgs a) {
   constexpr int BR = 128, BC = 64;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32;
-  __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];
-  __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
+  // each buffer its own object: the compiler orders a transposing LDS read
+  // after every pending direct-to-LDS load into the same object, which
+  // would make each tile wait for the next tile's prefetch
+  __shared__ __attribute__((aligned(1024))) T sK0[BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sK1[BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sV0[BC * DV];
+  __shared__ __attribute__((aligned(1024))) T sV1[BC * DV];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
@@ -598,8 +603,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   ldK.init(kg, a.sk_.s, w, lane);
   ldV.init(vg, a.sv_.s, w, lane);
   if (nt > 0) {
-    ldK.load(sK[0], t0 * BC, skv, w, lane);
-    ldV.load(sV[0], t0 * BC, skv, w, lane);
+    ldK.load(sK0, t0 * BC, skv, w, lane);
+    ldV.load(sV0, t0 * BC, skv, w, lane);
   }
   RowReader<DQK, T> rdK;
   RowReader<DV, T> rdV;
@@ -737,8 +742,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   };
 
   for (int it = 0; it < nt; it += 2) {
-    tile(it, sK[0], sV[0], sK[1], sV[1]);
-    if (it + 1 < nt) tile(it + 1, sK[1], sV[1], sK[0], sV[0]);
+    tile(it, sK0, sV0, sK1, sV1);
+    if (it + 1 < nt) tile(it + 1, sK1, sV1, sK0, sV0);
   }
 
   if (row_ok) {

@@ -23,23 +23,77 @@
 // Per 32-key tile a wave computes S^T = K Q^T and O^T += V^T P^T exactly as
 // the main forward does (sig-permuted K rows, transposing LDS reads of V),
 // with the same base-2 online softmax and lazy rescale.
+//
+// Q8: K and V arrive as int8 codes with one fp32 scale (and optionally one
+// int8 zero point) per token and group of head-dim elements - the grouped
+// key / value quantization of the oneDNN micro SDPA host driver.  The
+// codes stream into double-buffered int8 staging tiles (half the bytes),
+// each lane dequantizes 16-byte chunks, x = (code - zp) * scale, into one
+// 16-bit tile per operand, and the tile step above runs unchanged on it.
 #include <algorithm>
+#include <type_traits>
 
 #include "sdpa_kcommon.h"
 
 namespace sdpa {
 
-template <typename T, int DQK, int DV, bool BAND>
+// Dequantize one 32-row int8 tile (rows of D bytes, staged with the Lds<D/2>
+// layout of 16-bit elements) into a 16-bit tile (Lds<D> layout).  Lane l
+// converts 16-byte chunk l & (D/16 - 1) of rows (l / (D/16)) + (64 / (D/16)) u;
+// sc[u] / zp[u] are that chunk's scale and zero point.
+template <typename T, int D>
+__device__ __forceinline__ void dequant_tile(const uint16_t* src, T* dst, const float (&sc)[4],
+                                             const int (&zp)[4], int lane) {
+  constexpr int CPR = D / 16;  // 16-byte int8 chunks per row
+  constexpr int RPU = 64 / CPR;
+  static_assert(32 * CPR == 64 * 4, "four chunks per lane");
+  const int cc = lane & (CPR - 1);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = lane / CPR + RPU * u;
+    const u32x4 raw = lds_load16(lds_addr(src + Lds<D / 2>::off(row, 8 * cc)));
+    const float s = sc[u], o = -(float)zp[u] * sc[u];
+    uint32_t outw[8];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint32_t x = raw[wd];
+      float f[4];
+#pragma unroll
+      for (int by = 0; by < 4; ++by) f[by] = __builtin_fmaf((float)(int8_t)(x >> (8 * by)), s, o);
+      outw[2 * wd] = pack2<T>(f[0], f[1]);
+      outw[2 * wd + 1] = pack2<T>(f[2], f[3]);
+    }
+    *(u32x4*)(dst + Lds<D>::off(row, 16 * cc)) = u32x4{outw[0], outw[1], outw[2], outw[3]};
+    *(u32x4*)(dst + Lds<D>::off(row, 16 * cc + 8)) = u32x4{outw[4], outw[5], outw[6], outw[7]};
+  }
+}
+
+// QM: 0 = 16-bit K/V, 1 = int8 K/V with scales, 2 = int8 K/V with scales
+// and zero points
+template <typename T, int DQK, int DV, bool BAND, int QM>
 __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const DecodeArgs d) {
+  constexpr bool Q8 = QM != 0;
   constexpr int BC = 32;        // keys per wave tile
   constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
   constexpr int DB = DV / 32;   // 32-wide blocks of d_v
   constexpr float TAU = 8.f;
-  // per wave: two K and two V tiles; after the loop the wave's K region
-  // holds its partial O (32 x DV fp32) and its V region its row max / sum
-  static_assert(2 * BC * DQK * sizeof(T) >= 32 * DV * sizeof(float), "O partial must fit");
-  __shared__ __attribute__((aligned(1024))) T sK[4][2][BC * DQK];
-  __shared__ __attribute__((aligned(1024))) T sV[4][2][BC * DV];
+  // Per-wave LDS tiles, each buffer its own object: the compiler orders a
+  // transposing LDS read after every pending direct-to-LDS load into the
+  // same object, which would wait for the next tile's load.  16-bit io:
+  // K and V tiles double-buffered (sK0/sK1, sV0/sV1).  Q8: one dequantized
+  // K and V tile (sK0, sV0) and double-buffered int8 staging tiles.  After
+  // the loop, the wave's partial O (32 x DV fp32) is rows 0-15 in sK0 and
+  // rows 16-31 in sV0, its row max / sum in sK1 (sKq0 for Q8).
+  static_assert(!Q8 || (DQK == 128 && DV == 128), "int8 K/V: head dim 128");
+  static_assert(16 * DV * 4 <= BC * DV * 2, "half an O partial fits a V tile");
+  __shared__ __attribute__((aligned(1024))) T sK0[4][BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sK1[4][Q8 ? 1 : BC * DQK];
+  __shared__ __attribute__((aligned(1024))) T sV0[4][BC * DV];
+  __shared__ __attribute__((aligned(1024))) T sV1[4][Q8 ? 1 : BC * DV];
+  __shared__ __attribute__((aligned(1024))) uint16_t sKq0[4][Q8 ? BC * DQK / 2 : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t sKq1[4][Q8 ? BC * DQK / 2 : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t sVq0[4][Q8 ? BC * DV / 2 : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t sVq1[4][Q8 ? BC * DV / 2 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
@@ -90,20 +144,66 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   for (int t = 0; t < KT; ++t)
     qreg[t] = row_ok ? *(const u32x4*)(qrow + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
 
-  TileLoader<DQK, BC, T, 1> ldK;
-  TileLoader<DV, BC, T, 1> ldV;
-  ldK.init(base_ptr<T>(a.k, a.sk_, sp, hk, false), a.sk_.s, 0, lane);
-  ldV.init(base_ptr<T>(a.v, a.sv_, sp, hk, false), a.sv_.s, 0, lane);
-  if (ntw > 0) {
-    ldK.load(sK[w][0], (tb + w) * BC, skv, 0, lane);
-    ldV.load(sV[w][0], (tb + w) * BC, skv, 0, lane);
+  // tiles: LT is the 16-bit element type the loaders move (int8 rows are
+  // moved as rows of D/2 16-bit elements)
+  using LT = std::conditional_t<Q8, uint16_t, T>;
+  constexpr int LDQK = Q8 ? DQK / 2 : DQK, LDV = Q8 ? DV / 2 : DV;
+  T* const kd = sK0[w];  // Q8: dequantized K tile
+  T* const vd = sV0[w];  // Q8: dequantized V tile
+  // the tiles the loads fill (buf a compile-time constant)
+  auto ktile = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    if constexpr (Q8) return buf ? sKq1[w] : sKq0[w];
+    else return buf ? sK1[w] : sK0[w];
+  };
+  auto vtile = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    if constexpr (Q8) return buf ? sVq1[w] : sVq0[w];
+    else return buf ? sV1[w] : sV0[w];
+  };
+  TileLoader<LDQK, BC, LT, 1> ldK;
+  TileLoader<LDV, BC, LT, 1> ldV;
+  if constexpr (Q8) {
+    const int8_t* kq = (const int8_t*)a.k + sp.bsel * a.sk_.b + (int64_t)hk * a.sk_.h + sp.ktok * a.sk_.s;
+    const int8_t* vq = (const int8_t*)a.v + sp.bsel * a.sv_.b + (int64_t)hk * a.sv_.h + sp.ktok * a.sv_.s;
+    ldK.init((const LT*)kq, a.sk_.s / 2, 0, lane);
+    ldV.init((const LT*)vq, a.sv_.s / 2, 0, lane);
+  } else {
+    ldK.init(base_ptr<LT>(a.k, a.sk_, sp, hk, false), a.sk_.s, 0, lane);
+    ldV.init(base_ptr<LT>(a.v, a.sv_, sp, hk, false), a.sv_.s, 0, lane);
   }
-  if (ntw > 1) {
-    ldK.load(sK[w][1], (tb + w + 4) * BC, skv, 0, lane);
-    ldV.load(sV[w][1], (tb + w + 4) * BC, skv, 0, lane);
-  }
-  // loads of one tile (K and V), all direct-to-LDS
-  constexpr int TILE_LOADS = TileLoader<DQK, BC, T, 1>::PER_WAVE + TileLoader<DV, BC, T, 1>::PER_WAVE;
+  // Q8: this lane's scale / zero point column (its chunk's group) and the
+  // per-token scale rows of this sequence and key/value head
+  const int qcol = Q8 ? (16 * (lane & 7)) / d.qgs : 0;
+  const int64_t sc_base = sp.bsel * d.ss.b + (int64_t)hk * d.ss.h + sp.ktok * d.ss.s + qcol;
+  float ksc[2][4], vsc[2][4];
+  int kzp[2][4], vzp[2][4];
+  // (buf is a compile-time constant: the scale registers are indexed by it)
+  auto load_tile = [&](auto bufc, int n0) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    ldK.load(ktile(bufc), n0, skv, 0, lane);
+    ldV.load(vtile(bufc), n0, skv, 0, lane);
+    if constexpr (Q8) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
+        ksc[buf][u] = d.k_sc[sc_base + (int64_t)row * d.ss.s];
+        vsc[buf][u] = d.v_sc[sc_base + (int64_t)row * d.ss.s];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
+        kzp[buf][u] = QM == 2 ? d.k_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+        vzp[buf][u] = QM == 2 ? d.v_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+      }
+    }
+  };
+  if (ntw > 0) load_tile(std::integral_constant<int, 0>{}, (tb + w) * BC);
+  if (ntw > 1) load_tile(std::integral_constant<int, 1>{}, (tb + w + 4) * BC);
+  // vector memory operations of one tile (K and V direct-to-LDS loads, and
+  // the scales and zero points of int8 K/V)
+  constexpr int TILE_LOADS = TileLoader<LDQK, BC, LT, 1>::PER_WAVE +
+                             TileLoader<LDV, BC, LT, 1>::PER_WAVE + 8 * QM;
 
   const float c = a.scale_log2;
   // a zero scale cannot hide a score with an infinity through the FMA: such
@@ -122,13 +222,27 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   rdK.init(lane);
   rdV.init(lane);
 
-  // Tile j sits in buffer j % 2 (`cK`, `cV`); tile j + 1, if any, is in
-  // flight into the other buffer.
-  auto tile = [&](int j, T* cK, T* cV) __attribute__((always_inline)) {
+  // Tile j sits in buffer j % 2 == buf; tile j + 1, if any, is in flight
+  // into the other buffer.
+  auto tile = [&](int j, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int n0 = (tb + w + 4 * j) * BC;
     // tile j has landed (tile j + 1 may still be loading)
     if (j + 1 < ntw) wait_vm<TILE_LOADS>();
     else wait_vm<0>();
+    const T* cK;
+    const T* cV;
+    if constexpr (Q8) {
+      dequant_tile<T, DQK>(ktile(bufc), kd, ksc[buf], kzp[buf], lane);
+      dequant_tile<T, DV>(vtile(bufc), vd, vsc[buf], vzp[buf], lane);
+      wait_lds();  // the 16-bit tiles are written, the staging tiles read
+      if (j + 2 < ntw) load_tile(bufc, n0 + 8 * BC);
+      cK = kd;
+      cV = vd;
+    } else {
+      cK = (const T*)ktile(bufc);
+      cV = (const T*)vtile(bufc);
+    }
     u32x4 kop[KT], vop[2 * DB];
     static_for<KT>([&](auto t) __attribute__((always_inline)) { kop[t] = rdK.template read<t>(cK, 0); });
 #pragma unroll
@@ -136,10 +250,9 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
       static_for<DB>([&](auto db) __attribute__((always_inline)) {
         vop[tt * DB + db] = rdV.template read<32 * db>(cV, 16 * tt);
       });
-    if (j + 2 < ntw) {
+    if (!Q8 && j + 2 < ntw) {
       wait_lds();  // the operands are in registers: the buffers are free
-      ldK.load(cK, n0 + 8 * BC, skv, 0, lane);
-      ldV.load(cV, n0 + 8 * BC, skv, 0, lane);
+      load_tile(bufc, n0 + 8 * BC);
     }
     f32x16 s = f32x16{};
 #pragma unroll
@@ -200,23 +313,29 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   };
 
   for (int j = 0; j < ntw; j += 2) {
-    tile(j, sK[w][0], sV[w][0]);
-    if (j + 1 < ntw) tile(j + 1, sK[w][1], sV[w][1]);
+    tile(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntw) tile(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- merge the four waves' (max, sum, O) through LDS -----------------
   wait_all();
-  // [32 rows][DV] with 16-byte chunks XOR-swizzled by row (conflict-free
-  // column writes)
-  float* sOw = (float*)sK[w][0];
-  float* sMLw = (float*)sV[w][0];  // [32] max, then [32] sum
+  // rows of DV floats with 16-byte chunks XOR-swizzled by row
+  // (conflict-free column writes); rows 0-15 in sK0, 16-31 in sV0
+  auto orow_ptr = [&](int wv, int rl) __attribute__((always_inline)) {
+    return (float*)(rl < 16 ? (void*)sK0[wv] : (void*)sV0[wv]) + (rl & 15) * DV;
+  };
+  auto ml_ptr = [&](int wv) __attribute__((always_inline)) {
+    if constexpr (Q8) return (float*)sKq0[wv];
+    else return (float*)sK1[wv];
+  };
+  float* sMLw = ml_ptr(w);  // [32] max, then [32] sum
   const float l_row = sum_pair32(l_run);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int dd = 32 * db + 8 * rr + 4 * g;
-      *(f32x4*)(sOw + l32 * DV + ((((dd >> 2) ^ l32) & (DV / 4 - 1)) << 2)) =
+      *(f32x4*)(orow_ptr(w, l32) + ((((dd >> 2) ^ l32) & (DV / 4 - 1)) << 2)) =
           f32x4{oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]};
     }
   if (g == 0) {
@@ -232,14 +351,14 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
     if (rr_ >= nrows) break;  // rows are contiguous: the rest are past the end too
     float M = -1e30f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) M = fmaxf(M, ((const float*)sV[v][0])[rl]);
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_ptr(v)[rl]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float* ml = (const float*)sV[v][0];
+      const float* ml = ml_ptr(v);
       const float f = __builtin_amdgcn_exp2f(ml[rl] - M);
       L += f * ml[32 + rl];
-      O += f * ((const float*)sK[v][0])[rl * DV + ((((dd >> 2) ^ rl) & (DV / 4 - 1)) << 2) + (dd & 3)];
+      O += f * orow_ptr(v, rl)[((((dd >> 2) ^ rl) & (DV / 4 - 1)) << 2) + (dd & 3)];
     }
     const float o = L > 0.f ? O / L : 0.f;
     const float lse = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
@@ -320,8 +439,17 @@ template <typename T, int DQK, int DV>
 static hipError_t decode_dims(bool band, const FwdArgs& a, const DecodeArgs& d, hipStream_t st) {
   const int64_t units = (int64_t)a.B * (a.H / a.G) * d.ns * d.rg;
   dim3 grid((unsigned)(8 * ((units + 7) / 8))), block(256);
-  if (band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true>), grid, block, 0, st, a, d);
-  else hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false>), grid, block, 0, st, a, d);
+  const int qm = d.k_sc == nullptr ? 0 : (d.k_zp == nullptr ? 1 : 2);
+  if constexpr (DQK == 128 && DV == 128) {
+    if (qm == 1 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 1>), grid, block, 0, st, a, d);
+    if (qm == 1 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 1>), grid, block, 0, st, a, d);
+    if (qm == 2 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 2>), grid, block, 0, st, a, d);
+    if (qm == 2 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 2>), grid, block, 0, st, a, d);
+  } else if (qm != 0) {
+    return hipErrorInvalidValue;
+  }
+  if (qm == 0 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 0>), grid, block, 0, st, a, d);
+  if (qm == 0 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 0>), grid, block, 0, st, a, d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || d.ns == 1) return e;
   dim3 cgrid((unsigned)((d.nr + 3) / 4));

@@ -93,6 +93,13 @@ struct DecodeArgs {
   int32_t ns;       // splits
   int32_t chunk;    // keys per split, a multiple of 128
   int32_t rg;       // 32-row groups of (query head of the group, position) pairs
+  // int8 K/V (k_sc non-null; a.k, a.v then hold int8 codes with byte
+  // strides): per (token, group of qgs head-dim elements) fp32 scales and
+  // nullable int8 zero points, at element strides ss (group index unit)
+  const float *k_sc, *v_sc;
+  const int8_t *k_zp, *v_zp;
+  Str ss;
+  int32_t qgs;
 };
 struct DecodePlan {
   int32_t ns, chunk, rg;

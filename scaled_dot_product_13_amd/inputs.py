@@ -10,6 +10,14 @@ Q, K, V, [bias], dO as float32 standard normals, each then rounded to the io
 dtype (round to nearest even).  Tensors are dense BHSD (batch mode) or packed
 THD with cu_seqlens = [0, cumsum(lengths)] (group mode); K and V use the
 same lengths unless explicit key/value lengths are given.
+
+Quantized K/V (kv_quant = (group_size, with_zero_points)): K and V are int8
+codes clip(round(40 z), -127, 127), z standard normal, with fp32 scales
+U(0.02, 0.03) per token and group of head-dim elements (about what a
+per-group max-abs quantizer gives for N(0, 1) data) and, optionally, int8
+zero points randint(-8, 9); drawn in the order codes K, scales K, [zero
+points K], codes V, scales V, [zero points V], in place of the K and V
+normals.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -45,6 +53,7 @@ class Workload:
     bottom_right: bool = False
     window_left: Optional[int] = None
     window_right: Optional[int] = None
+    kv_quant: Optional[tuple] = None  # (group_size, with_zero_points): int8 K/V codes
     extra: dict = field(default_factory=dict)
 
     @property
@@ -71,6 +80,11 @@ WORKLOADS = {
 # head), bottom-right causal as a decoder step is.
 DECODE = Workload("bf16 decode B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1, 8192, 128, 128,
                   causal=True, bottom_right=True, h_kv=8, seed=1006)
+# The same step over an int8 K/V cache: scales per token and group of 32
+# head-dim elements, no zero points.
+DECODE_Q8 = Workload("bf16 decode int8-KV g32 B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1,
+                     8192, 128, 128, causal=True, bottom_right=True, h_kv=8, seed=1007,
+                     kv_quant=(32, False))
 
 
 def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
@@ -110,8 +124,18 @@ def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
         shp_v = (wl.b, hk, wl.s_kv, wl.d_v)
         shp_o = (wl.b, wl.h, wl.s_q, wl.d_v)
     out["q"] = torch.randn(shp_q, generator=g, dtype=torch.float32).to(io)
-    out["k"] = torch.randn(shp_k, generator=g, dtype=torch.float32).to(io)
-    out["v"] = torch.randn(shp_v, generator=g, dtype=torch.float32).to(io)
+    if wl.kv_quant is None:
+        out["k"] = torch.randn(shp_k, generator=g, dtype=torch.float32).to(io)
+        out["v"] = torch.randn(shp_v, generator=g, dtype=torch.float32).to(io)
+    else:
+        gs, with_zp = wl.kv_quant
+        for name, shp in (("k", shp_k), ("v", shp_v)):
+            z = torch.randn(shp, generator=g, dtype=torch.float32)
+            out[name] = torch.clamp(torch.round(40.0 * z), -127, 127).to(torch.int8)
+            sshp = shp[:-1] + (shp[-1] // gs,)
+            out[name + "_scales"] = 0.02 + 0.01 * torch.rand(sshp, generator=g, dtype=torch.float32)
+            out[name + "_zp"] = (torch.randint(-8, 9, sshp, generator=g).to(torch.int8)
+                                 if with_zp else None)
     if wl.bias:
         out["bias"] = torch.randn((wl.b, wl.h, wl.s_q, wl.s_kv), generator=g,
                                   dtype=torch.float32).to(io)
@@ -121,9 +145,9 @@ def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
 
 def small(dtype="bf16", b=1, h=2, s_q=200, s_kv=200, d_qk=128, d_v=128, causal=False,
           bias=False, dropout_p=0.0, seed=7, varlen=None, scale=None, h_kv=None,
-          bottom_right=False, window_left=None, window_right=None) -> Workload:
+          bottom_right=False, window_left=None, window_right=None, kv_quant=None) -> Workload:
     """A small workload (parity-test size) with the same recipe."""
     return Workload(f"small-{dtype}", dtype, b, h, s_q, s_kv, d_qk, d_v, causal=causal, bias=bias,
                     dropout_p=dropout_p, seed=seed, varlen=varlen, scale=scale, h_kv=h_kv,
                     bottom_right=bottom_right, window_left=window_left,
-                    window_right=window_right)
+                    window_right=window_right, kv_quant=kv_quant)

@@ -48,6 +48,10 @@ class Problem(ctypes.Structure):
         ("mask_flags", ctypes.c_uint32), ("window_left", ctypes.c_int64),
         ("window_right", ctypes.c_int64),
         ("alibi_slopes", ctypes.c_void_p), ("alibi_batch_stride", ctypes.c_int64),
+        ("kv_quant", ctypes.c_int32), ("kv_group_size", ctypes.c_int32),
+        ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_zero_points", ctypes.c_void_p), ("v_zero_points", ctypes.c_void_p),
+        ("kv_scale_strides", Strides),
     ]
 
 
@@ -136,7 +140,7 @@ def _stream():
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None,
-                 alibi_slopes=None):
+                 alibi_slopes=None, kv_scales=None, kv_zero_points=None, kv_group_size=None):
     """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group
     [T,H,D]); k and v may have fewer heads than q (grouped-query attention).
 
@@ -146,7 +150,12 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
 
     alibi_slopes: fp32 device tensor [B, H] (or [H], shared by the batch);
     adds -slope |j - i - off'| to the scores, off' the mask's alignment
-    (bottom-right without a mask).  The tensor must outlive the call."""
+    (bottom-right without a mask).  The tensor must outlive the call.
+
+    int8 K/V: k and v are int8 codes; kv_scales = (k_scales, v_scales),
+    fp32 [.., tokens, d / kv_group_size] laid out like k without its last
+    dimension (batch [B, Hkv, S, G] or group [T, Hkv, G]); kv_zero_points
+    likewise int8, or None."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     group = cu_seqlens_q is not None
@@ -176,6 +185,19 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
             raise TypeError("alibi_slopes must be a float32 tensor with unit stride along heads")
         p.alibi_slopes = alibi_slopes.data_ptr()
         p.alibi_batch_stride = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
+    if kv_scales is not None:
+        ks, vs = kv_scales
+        if ks.dtype != torch.float32 or vs.dtype != torch.float32 or ks.stride() != vs.stride():
+            raise TypeError("kv_scales: two float32 tensors with equal strides")
+        p.kv_quant = 1
+        p.kv_group_size = int(kv_group_size)
+        p.k_scales, p.v_scales = ks.data_ptr(), vs.data_ptr()
+        p.kv_scale_strides = _strides(ks, group)
+        if kv_zero_points is not None:
+            kz, vz = kv_zero_points
+            if kz.stride() != ks.stride() or vz.stride() != ks.stride():
+                raise TypeError("kv_zero_points must have the strides of kv_scales")
+            p.k_zero_points, p.v_zero_points = kz.data_ptr(), vz.data_ptr()
     p.dropout_probability = float(dropout_p)
     p.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     p.dropout_offset = int(offset) & 0xFFFFFFFFFFFFFFFF
@@ -187,7 +209,8 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
              seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
              max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None,
              bottom_right=False, window_left=None, window_right=None, split_kv=True,
-             workspace=None, alibi_slopes=None):
+             workspace=None, alibi_slopes=None, kv_scales=None, kv_zero_points=None,
+             kv_group_size=None):
     """Forward.  Returns (o, lse or None, keep or None).  split_kv=False
     passes no workspace, so a thin-query problem runs unsplit; `workspace`
     (uint8, at least fwd_workspace_size bytes) avoids an allocation."""
@@ -197,7 +220,8 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
                      cu_seqlens_kv=cu_seqlens_kv, max_seqlen_q=max_seqlen_q,
                      max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
                      window_left=window_left, window_right=window_right,
-                     alibi_slopes=alibi_slopes)
+                     alibi_slopes=alibi_slopes, kv_scales=kv_scales,
+                     kv_zero_points=kv_zero_points, kv_group_size=kv_group_size)
     if out is None:
         oshape = list(q.shape)
         oshape[-1] = v.shape[-1]

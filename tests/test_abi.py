@@ -58,6 +58,10 @@ def _problem(S, **kw):
     p.window_left, p.window_right = kw.get("window", (-1, -1))
     if "alibi" in kw:
         p.alibi_slopes, p.alibi_batch_stride = kw["alibi"]
+    if "q8" in kw:
+        p.kv_quant, p.kv_group_size = 1, kw["q8"]
+        p.k_scales = p.v_scales = FAKE
+        p.kv_scale_strides = S.Strides(2 * 64 * 8, 64 * 8, 8)
     return p
 
 
@@ -116,6 +120,17 @@ def test_invalid_arguments(S):
     assert _fwd(S, _problem(S, alibi=(FAKE, 2)), bias=FAKE) == S.SDPA_ERR_UNSUPPORTED
     assert b"alibi_slopes" in L.sdpa_last_error_message()
     assert _bwd(S, _problem(S, alibi=(FAKE, 0)), bias=FAKE) == S.SDPA_ERR_UNSUPPORTED
+    # int8 K/V: forward only, thin queries only, a supported group size
+    q8 = _problem(S, q8=32)
+    q8.kv_quant = 5
+    assert _fwd(S, q8) == S.SDPA_ERR_INVALID_ARG
+    assert _fwd(S, _problem(S, q8=32)) == S.SDPA_ERR_UNSUPPORTED  # s_q = 64 is not thin
+    assert b"thin-query" in L.sdpa_last_error_message()
+    assert _fwd(S, _problem(S, q8=24, s_q=1)) == S.SDPA_ERR_UNSUPPORTED
+    assert b"kv_group_size" in L.sdpa_last_error_message()
+    assert _fwd(S, _problem(S, q8=32, s_q=1, d_qk=64, d_v=64)) == S.SDPA_ERR_UNSUPPORTED
+    assert _bwd(S, _problem(S, q8=32, s_q=1)) == S.SDPA_ERR_UNSUPPORTED
+    assert b"forward" in L.sdpa_last_error_message()
 
 
 def test_problem_struct_matches_the_header(S):

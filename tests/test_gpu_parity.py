@@ -19,6 +19,11 @@ Tolerances (written here, used everywhere below):
                    forward's io-typed O while the oracle uses its fp64 O.
   LSE (all io)   : max|gpu - ref| <= 1e-3; rows that see no key: -inf on both
   keep mask      : bit-exact on every position the mask leaves visible
+  int8 K/V LSE   : |gpu - ref|_i <= 1e-3 + u scale max_j sum_c |Q_ic K_jc|.
+                   The kernel dequantizes K to the io type before its
+                   product, which moves each score by at most u scale
+                   sum_c |Q_ic K_jc| (u the io unit roundoff), and LSE, a
+                   smooth maximum, moves by at most the largest such shift.
 """
 import sys
 
@@ -368,6 +373,85 @@ def test_alibi_varlen(S):
     lengths, kv_lengths = [90, 1, 200], [150, 40, 200]
     wl = inputs.small("bf16", b=3, h=4, h_kv=2, d_qk=128, d_v=128, seed=37, varlen=(3, 1, 200))
     run_workload(S, wl, lengths=lengths, kv_lengths=kv_lengths, alibi=_alibi_slopes(3, 4, 37))
+
+
+def run_q8(S, wl, lengths=None, kv_lengths=None, split=True):
+    """Thin-query forward over int8 K/V codes against the oracle's forward on
+    the dequantized K and V (fp64)."""
+    x = inputs.make_inputs(wl, lengths, kv_lengths)
+    gs, with_zp = wl.kv_quant
+    group = wl.varlen is not None
+    dev = "cuda"
+    g = {n: x[n].to(dev) for n in ("q", "k", "v", "k_scales", "v_scales")}
+    zp = (x["k_zp"].to(dev), x["v_zp"].to(dev)) if with_zp else None
+    kw = dict(scale=wl.softmax_scale, causal=wl.causal, bottom_right=wl.bottom_right,
+              window_left=wl.window_left, window_right=wl.window_right)
+    okw = dict(kw)
+    if group:
+        kw.update(cu_seqlens_q=x["cu_seqlens"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
+                  max_seqlen_q=x["max_seqlen"], max_seqlen_kv=x["max_seqlen_kv"])
+        okw.update(cu_seqlens_q=x["cu_seqlens"].numpy().astype(np.int64),
+                   cu_seqlens_kv=x["cu_seqlens_kv"].numpy().astype(np.int64))
+    _say("int8 K/V", wl.dtype, "B", wl.b, "H", wl.h, "Hkv", wl.h_kv, "Sq", wl.s_q, "Skv", wl.s_kv,
+         "group size", gs, "zero points", with_zp, "varlen", group, "split", split, kw.get("causal"))
+    o, lse, _ = S.sdpa_fwd(g["q"], g["k"], g["v"], kv_scales=(g["k_scales"], g["v_scales"]),
+                           kv_zero_points=zp, kv_group_size=gs, split_kv=split, **kw)
+    torch.cuda.synchronize()
+    deq = {n: O.dequantize_kv(x[n].numpy(), x[n + "_scales"].numpy(), gs,
+                              x[n + "_zp"].numpy() if with_zp else None) for n in ("k", "v")}
+    ref = O.fwd(x["q"].double().numpy(), deq["k"], deq["v"], **okw)
+    errs = {"o": _cmp("o", _np(o), ref["o"], x["dtype"])}
+    # LSE: the bound of the module docstring, row by row
+    qf = x["q"].double().numpy()
+    r = wl.h // wl.h_kv
+    kf = np.repeat(deq["k"], r, axis=-2 if group else 1)
+    if group:
+        cu, cuk = x["cu_seqlens"].numpy(), x["cu_seqlens_kv"].numpy()
+        bound = np.zeros(ref["lse"].shape)
+        for b in range(len(cu) - 1):
+            qa = np.abs(qf[cu[b]:cu[b + 1]]).transpose(1, 0, 2)      # [H, sq, D]
+            ka = np.abs(kf[cuk[b]:cuk[b + 1]]).transpose(1, 2, 0)    # [H, D, skv]
+            bound[:, cu[b]:cu[b + 1]] = (qa @ ka).max(-1) if ka.shape[-1] else 0.0
+    else:
+        bound = (np.abs(qf) @ np.abs(kf).transpose(0, 1, 3, 2)).max(-1)
+    u = UNIT_ROUNDOFF[x["dtype"]]
+    got, want = _np(lse), ref["lse"]
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    fin = ~np.isneginf(want)
+    excess = np.abs(got - want)[fin] - (TOL_LSE + u * wl.softmax_scale * bound[fin])
+    errs["lse"] = float(np.max(np.abs(got - want)[fin])) if fin.any() else 0.0
+    assert float(np.max(excess, initial=-1.0)) <= 0, ("lse", errs["lse"])
+    _say("max errors", errs)
+    return errs
+
+
+Q8 = [
+    # dtype, s_q, s_kv, h, h_kv, group size, zero points, causal, window_left, split
+    ("bf16", 1, 1000, 8, 2, 32, False, True, None, True),
+    ("f16", 4, 777, 8, 2, 16, True, True, 100, True),
+    ("bf16", 16, 2081, 16, 2, 128, True, True, None, False),  # 4 row groups, unsplit
+    ("bf16", 1, 17, 4, 1, 64, False, False, None, True),
+    ("f16", 3, 600, 6, 3, 32, False, False, None, True),
+]
+
+
+@pytest.mark.parametrize("case", Q8, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-h{c[3]}kv{c[4]}-g{c[5]}"
+                         f"-zp{int(c[6])}-c{int(c[7])}-w{c[8]}-split{int(c[9])}")
+def test_int8_kv_thin_query_parity(S, case):
+    dt, sq, skv, h, hkv, gs, zp, causal, wl_, split = case
+    wl = inputs.small(dt, b=2, h=h, h_kv=hkv, s_q=sq, s_kv=skv, causal=causal, bottom_right=True,
+                      window_left=wl_, seed=sq * 13 + skv, kv_quant=(gs, zp))
+    run_q8(S, wl, split=split)
+
+
+def test_int8_kv_varlen(S):
+    wl = inputs.small("bf16", b=3, h=8, h_kv=2, causal=True, bottom_right=True, seed=41,
+                      varlen=(3, 1, 1), kv_quant=(32, True))
+    run_q8(S, wl, lengths=[1, 1, 2], kv_lengths=[1, 700, 3000])
+
+
+def test_int8_kv_decode_workload_full(S):
+    run_q8(S, inputs.DECODE_Q8)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
