@@ -176,6 +176,9 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   // per-token scale rows of this sequence and key/value head
   const int qcol = Q8 ? (16 * (lane & 7)) / d.qgs : 0;
   const int64_t sc_base = sp.bsel * d.ss.b + (int64_t)hk * d.ss.h + sp.ktok * d.ss.s + qcol;
+  // this lane's scale (zero point) entries for tile row lane / 8; a tile's
+  // row u-th group then only adds the uniform (n0 + 8u) rows
+  const int64_t sc_lane = sc_base + (int64_t)(lane >> 3) * d.ss.s;
   float ksc[2][4], vsc[2][4];
   int kzp[2][4], vzp[2][4];
   // (buf is a compile-time constant: the scale registers are indexed by it)
@@ -184,17 +187,34 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
     ldK.load(ktile(bufc), n0, skv, 0, lane);
     ldV.load(vtile(bufc), n0, skv, 0, lane);
     if constexpr (Q8) {
+      if (n0 + BC <= skv) {
+        // whole tile in range: per-lane offset plus a uniform row offset
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
-        ksc[buf][u] = d.k_sc[sc_base + (int64_t)row * d.ss.s];
-        vsc[buf][u] = d.v_sc[sc_base + (int64_t)row * d.ss.s];
-      }
+        for (int u = 0; u < 4; ++u) {
+          const int64_t o = sc_lane + (int64_t)(n0 + 8 * u) * d.ss.s;
+          ksc[buf][u] = d.k_sc[o];
+          vsc[buf][u] = d.v_sc[o];
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
-        kzp[buf][u] = QM == 2 ? d.k_zp[sc_base + (int64_t)row * d.ss.s] : 0;
-        vzp[buf][u] = QM == 2 ? d.v_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+        for (int u = 0; u < 4; ++u) {
+          const int64_t o = sc_lane + (int64_t)(n0 + 8 * u) * d.ss.s;
+          kzp[buf][u] = QM == 2 ? d.k_zp[o] : 0;
+          vzp[buf][u] = QM == 2 ? d.v_zp[o] : 0;
+        }
+      } else {
+        // the last tile: rows clamped to the sequence (those keys are masked)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
+          ksc[buf][u] = d.k_sc[sc_base + (int64_t)row * d.ss.s];
+          vsc[buf][u] = d.v_sc[sc_base + (int64_t)row * d.ss.s];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
+          kzp[buf][u] = QM == 2 ? d.k_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+          vzp[buf][u] = QM == 2 ? d.v_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+        }
       }
     }
   };
