@@ -134,6 +134,108 @@ def decode_bench(S, torch, steps, warmup, wl):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def _timed(torch, stream, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls, each bracketed by HIP events on
+    the launch stream, after `warmup` untimed calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+
+def suite_bench(S, torch, steps, warmup):
+    """The other workloads of the suite (fp16 with bias and dBias; bf16 packed
+    variable-length causal; bf16 causal with dropout): sdpa_fwd and the whole
+    sdpa_bwd, each timed with HIP events per call.  Reported as TFLOP/s of
+    the workload's algorithmic flop count and as GB/s of algorithmic HBM
+    bytes (inputs read once, outputs written once).  Also the standalone
+    backward preprocess (D = rowsum(dO o O) and LSE*log2(e)), an HBM-bound
+    kernel, on the headline and the variable-length shapes."""
+    from scaled_dot_product_13_amd import inputs
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for idx in (3, 4, 5):
+        wl = inputs.WORKLOADS[idx]
+        x = inputs.make_inputs(wl)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+        kw = dict(scale=wl.softmax_scale, causal=wl.causal)
+        e2 = q.element_size()
+        if wl.varlen is not None:
+            lens = [int(t) for t in x["lengths"]]
+            kw.update(cu_seqlens_q=x["cu_seqlens"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
+                      max_seqlen_q=x["max_seqlen"], max_seqlen_kv=x["max_seqlen_kv"])
+            pairs = sum(wl.h * L * L for L in lens)
+            rows = wl.h * sum(lens)
+            rows_kv = rows
+        else:
+            pairs = wl.b * wl.h * wl.s_q * wl.s_kv
+            rows = wl.b * wl.h * wl.s_q
+            rows_kv = wl.b * (wl.h_kv or wl.h) * wl.s_kv
+        if wl.causal:
+            pairs /= 2
+        if wl.dropout_p:
+            kw.update(dropout_p=wl.dropout_p, seed=inputs.DROPOUT_SEED, offset=0)
+        bias = x["bias"].to(dev) if wl.bias else None
+        del x
+        o, lse, _ = S.sdpa_fwd(q, k, v, bias=bias, **kw)
+        ws = torch.empty(max(1, S.bwd_workspace_size(q, k, v, **kw)), dtype=torch.uint8, device=dev)
+        f_ms = _timed(torch, stream, lambda: S.sdpa_fwd(q, k, v, bias=bias, out=o, lse=lse, **kw),
+                      steps, warmup)
+        b_ms = _timed(torch, stream, lambda: S.sdpa_bwd(q, k, v, o, do, lse, bias=bias,
+                                                        want_dbias=bias is not None,
+                                                        workspace=ws, **kw), steps, warmup)
+        f_fl = 2.0 * pairs * (wl.d_qk + wl.d_v)
+        b_fl = 2.0 * pairs * (3 * wl.d_qk + 2 * wl.d_v)
+        bias_b = bias.numel() * bias.element_size() if bias is not None else 0
+        f_by = (rows * wl.d_qk + rows_kv * (wl.d_qk + wl.d_v)) * e2 + bias_b + rows * wl.d_v * e2 + 4 * rows
+        b_by = ((rows * wl.d_qk + rows_kv * (wl.d_qk + wl.d_v) + 2 * rows * wl.d_v) * e2 + 4 * rows
+                + bias_b                                                         # in
+                + (rows * wl.d_qk + rows_kv * (wl.d_qk + wl.d_v)) * e2 + bias_b)  # dQ, dK, dV, dBias
+        out[str(idx)] = {
+            "workload": wl.name,
+            "fwd": {"ms": round(f_ms, 5), "tflops": round(f_fl / f_ms / 1e9, 2),
+                    "hbm_gbs": round(f_by / f_ms / 1e6, 1), "bytes": int(f_by)},
+            "bwd": {"ms": round(b_ms, 5), "tflops": round(b_fl / b_ms / 1e9, 2),
+                    "hbm_gbs": round(b_by / b_ms / 1e6, 1), "bytes": int(b_by)},
+            "tflops": round((f_fl + b_fl) / (f_ms + b_ms) / 1e9, 2),
+        }
+        if idx == 4:
+            # the standalone preprocess in group mode
+            n_st, off_st = S.stats_layout(len(lens), wl.h, kw["max_seqlen_q"])
+            st = torch.empty(off_st + n_st, dtype=torch.float32, device=dev)
+            p_ms = _timed(torch, stream, lambda: S.sdpa_bwd_preprocess(
+                o, do, lse, cu_seqlens_q=kw["cu_seqlens_q"], max_seqlen_q=kw["max_seqlen_q"], out=st),
+                steps, warmup)
+            p_by = 2 * rows * wl.d_v * e2 + 4 * rows + 8 * rows
+            out[str(idx)]["bwd_preprocess"] = {"ms": round(p_ms, 5), "bytes": int(p_by),
+                                               "hbm_gbs": round(p_by / p_ms / 1e6, 1)}
+        del q, k, v, do, o, lse, bias, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def preprocess_bench(S, torch, steps, warmup, q, o, do, lse, stats):
+    """The standalone backward preprocess on the headline shape (HBM-bound):
+    reads O, dO (io type) and LSE, writes D and LSE*log2(e) (fp32)."""
+    stream = torch.cuda.current_stream()
+    ms = _timed(torch, stream, lambda: S.sdpa_bwd_preprocess(o, do, lse, out=stats), steps, warmup)
+    rows = lse.numel()
+    by = 2 * o.numel() * o.element_size() + 4 * rows + 8 * rows
+    gbs = by / ms / 1e6
+    return {"ms": round(ms, 5), "bytes": int(by),
+            "roofline": {"kernel": "bwd_pre", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +244,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="workload index (2 = headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the thin-query (decode) line")
+    ap.add_argument("--no-suite", action="store_true",
+                    help="skip the other workloads and the standalone preprocess")
     ap.add_argument("--cpu-heads", type=int, default=1 << 30,
                     help="(batch, head) slices the CPU baseline times (default: all)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -274,6 +378,10 @@ def main():
                           "roofline kernel",
         "roofline": roof,
     }
+    if not args.no_suite:
+        ns, nw = min(args.steps, 20), min(args.warmup, 5)
+        out["bwd_preprocess"] = preprocess_bench(S, torch, ns, nw, q, o, do, lse, stats)
+        out["suite"] = suite_bench(S, torch, ns, nw)
     if not args.no_decode:
         out["decode"] = decode_bench(S, torch, args.steps, args.warmup, inputs.DECODE)
         out["decode_int8"] = decode_bench(S, torch, args.steps, args.warmup, inputs.DECODE_Q8)

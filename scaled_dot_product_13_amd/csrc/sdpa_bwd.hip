@@ -24,6 +24,9 @@
 #include "sdpa_kcommon.h"
 
 // heads whose tiles are interleaved rank-major on one XCD (see xcd_work)
+#ifndef SDPA_DKDV_BIAS_LDS_MAXD
+#define SDPA_DKDV_BIAS_LDS_MAXD 192
+#endif
 #ifndef SDPA_DKDV_HEAD_GROUP
 #define SDPA_DKDV_HEAD_GROUP 2
 #endif
@@ -97,7 +100,7 @@ template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   constexpr int BC = 128, BQ = 32, NSET = 3;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
-  constexpr bool BIAS_LDS = BIAS && DQK <= 128;
+  constexpr bool BIAS_LDS = BIAS && DQK <= SDPA_DKDV_BIAS_LDS_MAXD;
   // Query-side tiles are triple-buffered: role A reads set i % 3, role B
   // set (i - 1) % 3 and set (i + 1) % 3 is loading.
   __shared__ __attribute__((aligned(1024))) T sQ[NSET][BQ * DQK];

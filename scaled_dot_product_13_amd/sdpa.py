@@ -278,6 +278,12 @@ def fwd_workspace_size(q, k, v, **kw):
     return _lib.sdpa_fwd_workspace_size(ctypes.byref(make_problem(q, k, v, **kw)))
 
 
+def bwd_workspace_size(q, k, v, **kw):
+    """Bytes of backward workspace for these tensors and options (see
+    make_problem)."""
+    return _lib.sdpa_bwd_workspace_size(ctypes.byref(make_problem(q, k, v, **kw)))
+
+
 def stats_layout(b, h, s_q):
     """(n, offset) of the backward stats: D at [0, n), LSE*log2(e) at
     [offset, offset + n) floats (offset = n rounded up to 64 floats)."""
