@@ -628,6 +628,22 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
     // [n0 - (wq0 + 31), n0 + BC - 1 - wq0]
     const bool active = !BAND || (n0 - (wq0 + 31) <= bd.hi && n0 + BC - 1 - wq0 >= bd.lo);
 
+    if (it + 1 < nt) {
+      ldK.load(nK, n0 + BC, skv, w, lane);
+      ldV.load(nV, n0 + BC, skv, w, lane);
+    }
+    if (!active) return;
+
+    // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    static_for<KT>([&](auto t) __attribute__((always_inline)) {
+      const u32x4 a0 = rdK.template read<t>(cK, 0), a1 = rdK.template read<t>(cK, 32);
+      s[0] = mfma32<T>(a0, qreg[t], s[0]);
+      s[1] = mfma32<T>(a1, qreg[t], s[1]);
+    });
+    // bias for this lane's row, runs of 8 consecutive keys: requested
+    // between the two products, so that the dP products hide their latency
+    // without the registers being held across the score products too
     uint32_t braw[4][4];
     if (BIAS && active && !alibi) {
 #pragma unroll
@@ -647,19 +663,6 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
         }
       }
     }
-    if (it + 1 < nt) {
-      ldK.load(nK, n0 + BC, skv, w, lane);
-      ldV.load(nV, n0 + BC, skv, w, lane);
-    }
-    if (!active) return;
-
-    // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    static_for<KT>([&](auto t) __attribute__((always_inline)) {
-      const u32x4 a0 = rdK.template read<t>(cK, 0), a1 = rdK.template read<t>(cK, 32);
-      s[0] = mfma32<T>(a0, qreg[t], s[0]);
-      s[1] = mfma32<T>(a1, qreg[t], s[1]);
-    });
     static_for<VT>([&](auto t) __attribute__((always_inline)) {
       const u32x4 a0 = rdV.template read<t>(cV, 0), a1 = rdV.template read<t>(cV, 32);
       dp[0] = mfma32<T>(a0, doreg[t], dp[0]);
