@@ -17,6 +17,8 @@
 // V tile in LDS with the gfx950 transposing LDS read.  Softmax runs in base
 // 2 with log2(e) folded into the scale (CK stores scale*log2e beside the raw
 // scale in its kernel arguments).
+#include <type_traits>
+
 #include "sdpa_kcommon.h"
 
 #ifndef SDPA_FWD_NBLK
@@ -116,10 +118,38 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   rdK.init(lane);
   rdV.init(lane);
 
+  // Bias loads.  One-wave-per-SIMD instances (BIAS_PF) have the registers
+  // to hold a second tile's bias and request it one tile ahead; the latency
+  // of HBM loads is otherwise exposed there, with no other wave to run.
+  constexpr bool BIAS_PF = BIAS && FwdOcc<DQK, DV, DROP>::value == 1;
+  uint32_t bq[BIAS_PF ? 2 : 1][2 * NBLK][4];
+  auto load_bias = [&](uint32_t (&dst)[2 * NBLK][4], int nb) __attribute__((always_inline)) {
+    if (!BIAS || alibi) return;
+#pragma unroll
+    for (int u = 0; u < 2 * NBLK; ++u) {
+      int kb = nb + 16 * u + 8 * g;  // u = 2*blk + hh
+      const uint16_t* p = bg + (int64_t)row * a.sb_.s + kb;
+      if (row_ok && kb + 8 <= skv && a.bias_vec) {
+        u32x4 x = *(const u32x4*)p;
+        dst[u][0] = x[0]; dst[u][1] = x[1]; dst[u][2] = x[2]; dst[u][3] = x[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t lo = (row_ok && kb + 2 * e < skv) ? p[2 * e] : 0;
+          uint32_t hi = (row_ok && kb + 2 * e + 1 < skv) ? p[2 * e + 1] : 0;
+          dst[u][e] = lo | (hi << 16);
+        }
+      }
+    }
+  };
+  if (BIAS_PF && nt > 0) load_bias(bq[0], t0 * BC);
+
   // One key tile: `cK`, `cV` hold tile `it`; the next tile is loaded into
   // `nK`, `nV`.  Called with the two buffers swapped on alternate tiles so
-  // that every LDS address is a compile-time offset from a per-lane base.
-  auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV) __attribute__((always_inline)) {
+  // that every LDS address is a compile-time offset from a per-lane base
+  // (PC, the tile's parity, likewise selects the bias registers).
+  auto tile = [&](int it, const T* cK, const T* cV, T* nK, T* nV, auto pcc) __attribute__((always_inline)) {
+    constexpr int PC = decltype(pcc)::value;
     const int n0 = (t0 + it) * BC;
     wait_all();       // this wave's part of tile `it` has landed
     __syncthreads();  // ... and everyone's; tile it-1 is fully consumed
@@ -138,26 +168,16 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
       });
     }
 
-    // bias for this lane's row: runs of 8 consecutive keys (issued before
-    // the next tile's prefetch so that waiting for them does not wait for it)
-    uint32_t braw[2 * NBLK][4];
-    if (BIAS && active && !alibi) {
-#pragma unroll
-      for (int u = 0; u < 2 * NBLK; ++u) {
-        int kb = n0 + 16 * u + 8 * g;  // u = 2*blk + hh
-        const uint16_t* p = bg + (int64_t)row * a.sb_.s + kb;
-        if (row_ok && kb + 8 <= skv && a.bias_vec) {
-          u32x4 x = *(const u32x4*)p;
-          braw[u][0] = x[0]; braw[u][1] = x[1]; braw[u][2] = x[2]; braw[u][3] = x[3];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint32_t lo = (row_ok && kb + 2 * e < skv) ? p[2 * e] : 0;
-            uint32_t hi = (row_ok && kb + 2 * e + 1 < skv) ? p[2 * e + 1] : 0;
-            braw[u][e] = lo | (hi << 16);
-          }
-        }
-      }
+    // bias for this lane's row: runs of 8 consecutive keys.  With BIAS_PF
+    // the next tile's are requested here (they land with its K/V tiles);
+    // otherwise this tile's, before the next tile's prefetch so that
+    // waiting for them does not wait for it.
+    uint32_t braw_here[2 * NBLK][4];
+    uint32_t (&braw)[2 * NBLK][4] = *(BIAS_PF ? &bq[PC % (BIAS_PF ? 2 : 1)] : &braw_here);
+    if constexpr (BIAS_PF) {
+      if (it + 1 < nt) load_bias(bq[(1 - PC) % (BIAS_PF ? 2 : 1)], n0 + BC);
+    } else if (BIAS && active && !alibi) {
+      load_bias(braw, n0);
     }
     if (it + 1 < nt) {
       ldK.load(nK, n0 + BC, skv, w, lane);
@@ -317,8 +337,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   };
 
   for (int it = 0; it < nt; it += 2) {
-    tile(it, sK[0], sV[0], sK[1], sV[1]);
-    if (it + 1 < nt) tile(it + 1, sK[1], sV[1], sK[0], sV[0]);
+    tile(it, sK[0], sV[0], sK[1], sV[1], std::integral_constant<int, 0>{});
+    if (it + 1 < nt) tile(it + 1, sK[1], sV[1], sK[0], sV[0], std::integral_constant<int, 1>{});
   }
 
   // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2
