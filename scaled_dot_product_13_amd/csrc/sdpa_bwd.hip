@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   // one workgroup per (batch, key/value head, key tile); it accumulates dK,
   // dV over the query tiles of every query head of the head's group
   const int G = a.G;
-  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H / G, a.B, SDPA_DKDV_HEAD_GROUP);
+  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H / G, a.B, SDPA_DKDV_HEAD_GROUP, a.seq.cu_q != nullptr);
   if (!wi.valid) return;
   const int b = wi.b, hk = wi.h;
   const SeqPos sp = resolve_seq(a.seq, b);
@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(co
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_DQ_HEAD_GROUP);
+  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_DQ_HEAD_GROUP, a.seq.cu_q != nullptr);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest top-left causal tiles first

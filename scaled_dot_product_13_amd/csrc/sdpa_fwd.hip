@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP);
+  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, a.seq.cu_q != nullptr);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
