@@ -502,8 +502,12 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
 //   S^T = K Q^T,  dP^T = V dO^T   (A operands: K, V rows from LDS)
 //   dS^T = P^T o (dP^T - D)       (one query row per lane)
 //   dQ^T += K^T dS^T              (A = K^T via the transposing LDS read)
-template <int DQK, int DV, bool DROP> struct DqOcc {
-  static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
+// Two waves per SIMD (256 registers) unless the head dims are wide.  With
+// dropout the d 128 instances spill at that budget; the causal ones without
+// bias still run faster at two waves (measured), the others keep one wave.
+template <int DQK, int DV, bool DROP, bool BAND = false, bool BIAS = false> struct DqOcc {
+  static constexpr int value =
+      (DQK + DV > 256) || (DROP && DQK + DV > 128 && !(BAND && !BIAS)) ? 1 : 2;
 };
 
 //
@@ -511,7 +515,7 @@ template <int DQK, int DV, bool DROP> struct DqOcc {
 // and dO rows it loads and LSE*log2(e) from the forward's LSE, both written
 // to the stats for the dK/dV kernel, which then runs after it.
 template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP, bool PRE>
-__global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP>::value)) dq_mfma(const BwdArgs a) {
+__global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)) dq_mfma(const BwdArgs a) {
   constexpr int BR = 128, BC = 64;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32;
   // each buffer its own object: the compiler orders a transposing LDS read

@@ -32,12 +32,16 @@
 namespace sdpa {
 
 // workgroups per CU the register budget is sized for
-template <int DQK, int DV, bool DROP> struct FwdOcc {
-  static constexpr int value = (DQK + DV > 256 || DROP) ? 1 : 2;
+// Two waves per SIMD (256 registers) unless the head dims are wide.  With
+// dropout the d 128 instances spill at that budget; the causal ones without
+// bias still run faster at two waves (measured), the others keep one wave.
+template <int DQK, int DV, bool DROP, bool BAND = false, bool BIAS = false> struct FwdOcc {
+  static constexpr int value =
+      (DQK + DV > 256) || (DROP && DQK + DV > 128 && !(BAND && !BIAS)) ? 1 : 2;
 };
 
 template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
-__global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(const FwdArgs a) {
+__global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value)) fwd_mfma(const FwdArgs a) {
   constexpr int BR = 128;
   constexpr int NBLK = SDPA_FWD_NBLK;  // 32-key blocks per key tile
   constexpr int BC = 32 * NBLK;
@@ -121,7 +125,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP>::value)) fwd_mfma(
   // Bias loads.  One-wave-per-SIMD instances (BIAS_PF) have the registers
   // to hold a second tile's bias and request it one tile ahead; the latency
   // of HBM loads is otherwise exposed there, with no other wave to run.
-  constexpr bool BIAS_PF = BIAS && FwdOcc<DQK, DV, DROP>::value == 1;
+  constexpr bool BIAS_PF = BIAS && FwdOcc<DQK, DV, DROP, BAND, BIAS>::value == 1;
   uint32_t bq[BIAS_PF ? 2 : 1][2 * NBLK][4];
   auto load_bias = [&](uint32_t (&dst)[2 * NBLK][4], int nb) __attribute__((always_inline)) {
     if (!BIAS || alibi) return;
