@@ -561,6 +561,29 @@ def test_split_backward_equals_sdpa_bwd(S):
         assert torch.max(torch.abs(a_.float() - b_.float())).item() <= 2e-3
 
 
+@pytest.mark.parametrize("s_kv", [201, 131])
+def test_dbias_padded_rows_equal_dense(S, s_kv):
+    # dBias written into a padded tensor (row stride s_kv + 1) holds the same
+    # bits as the dense one (row stride s_kv, odd here) and leaves the
+    # padding column untouched; dK and dV do not depend on the dBias layout.
+    wl = inputs.small("bf16", b=1, h=2, s_q=96, s_kv=s_kv, bias=True, seed=57)
+    x = inputs.make_inputs(wl)
+    q, k, v, do, bias = (x[n].cuda() for n in ("q", "k", "v", "dout", "bias"))
+    kw = dict(causal=False)
+    _say("dbias padded rows", "s_kv", s_kv)
+    o, lse, _ = S.sdpa_fwd(q, k, v, bias=bias, **kw)
+    _, stats = S.sdpa_bwd_dq_preprocess(q, k, v, o, do, lse, bias=bias, **kw)
+    dk1, dv1, db1 = S.sdpa_bwd_dkdv(q, k, v, do, stats, bias=bias, want_dbias=True, **kw)
+    pad = torch.full((1, 2, 96, s_kv + 1), 7.0, dtype=bias.dtype, device="cuda")
+    dbp = pad[..., :s_kv]
+    dk2, dv2, db2 = S.sdpa_bwd_dkdv(q, k, v, do, stats, bias=bias, dbias=dbp, **kw)
+    torch.cuda.synchronize()
+    assert db1.stride(-2) == s_kv and dbp.stride(-2) == s_kv + 1
+    assert torch.equal(db1, db2)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    assert torch.all(pad[..., s_kv] == 7.0)
+
+
 def test_fused_preprocess_stats_group_mode(S):
     # the dQ kernel's own stats in group (varlen) mode equal the separate
     # preprocess's up to the fp32 rounding of D
