@@ -282,12 +282,22 @@ def main():
     # the GPU runs the headline's warm-up and timed steps near its steady
     # clocks: from an idle GPU, 10 warm-up steps (a few milliseconds of work)
     # leave the timed steps ~7% slower than 200 warm-up steps do.
+    def extra(fn, *a):
+        """A secondary measurement: an exception is reported in its place
+        rather than stopping the headline measurement."""
+        try:
+            return fn(*a)
+        except Exception as e:  # noqa: BLE001 - reported in the JSON line
+            print(f"bench.py: {fn.__name__} failed: {e!r}", file=sys.stderr, flush=True)
+            return {"error": repr(e)}
+
     decode = {}
     if not args.no_decode:
-        decode["decode"] = decode_bench(S, torch, args.steps, min(args.warmup, 10), inputs.DECODE)
-        decode["decode_int8"] = decode_bench(S, torch, args.steps, min(args.warmup, 10), inputs.DECODE_Q8)
+        decode["decode"] = extra(decode_bench, S, torch, args.steps, min(args.warmup, 10), inputs.DECODE)
+        decode["decode_int8"] = extra(decode_bench, S, torch, args.steps, min(args.warmup, 10),
+                                      inputs.DECODE_Q8)
     ns, nw = min(args.steps, 20), min(args.warmup, 5)
-    suite = suite_bench(S, torch, ns, nw) if not args.no_suite else None
+    suite = extra(suite_bench, S, torch, ns, nw) if not args.no_suite else None
 
     names = ("fwd", "bwd_dq", "bwd_dkdv")
     calls = (lambda: S.sdpa_fwd(q, k, v, out=o, lse=lse, **kw),
@@ -391,7 +401,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_suite:
-        out["bwd_preprocess"] = preprocess_bench(S, torch, ns, nw, q, o, do, lse, stats)
+        out["bwd_preprocess"] = extra(preprocess_bench, S, torch, ns, nw, q, o, do, lse, stats)
         out["suite"] = suite
     if not args.no_decode:
         out.update(decode)
