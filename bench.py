@@ -68,6 +68,20 @@ def stored_traffic(kernel):
         return None
 
 
+def cpu_info():
+    """Host facts for the CPU baseline: logical CPUs and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(wl, x, budget_heads):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: the first `budget_heads` (batch, head) slices in batch-major
@@ -85,15 +99,36 @@ def cpu_baseline(wl, x, budget_heads):
     f, b = flops(wl)
     frac = len(heads) / (wl.b * wl.h)
     return {"value": round((f + b) * frac / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
-            "kind": "oracle",
+            "kind": "oracle", **cpu_info(),
             "sample": f"fwd+bwd of {len(heads)} of {wl.b * wl.h} (batch, head) slices of the "
                       f"same workload, fp64, {dt:.1f} s wall"}
 
 
-def decode_bench(S, torch, steps, warmup, wl):
+class CacheFlush:
+    """Writes a 512 MiB device buffer, so that neither the 256 MB Infinity
+    Cache nor the L2s hold any input of the next call.  Called before each
+    timed iteration of the memory-bound measurements, outside the interval
+    the events bracket."""
+
+    def __init__(self, torch, dev, mib=512):
+        self.buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def decode_bench(S, torch, steps, warmup, wl, flush):
     """Time the thin-query forward on a decode workload: HIP events on the
     launch stream around each sdpa_fwd call (the split kernel and, when the
-    keys are split, the combine kernel)."""
+    keys are split, the combine kernel), the caches flushed before each
+    call; the median is reported."""
     from scaled_dot_product_13_amd import inputs
     x = inputs.make_inputs(wl)
     dev = torch.device("cuda:0")
@@ -113,45 +148,37 @@ def decode_bench(S, torch, steps, warmup, wl):
     lse = torch.empty((wl.b, wl.h, wl.s_q), dtype=torch.float32, device=dev)
     ws = torch.empty(max(S.fwd_workspace_size(q, k, v, **kw), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        S.sdpa_fwd(q, k, v, out=o, lse=lse, workspace=ws, **kw)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        S.sdpa_fwd(q, k, v, out=o, lse=lse, workspace=ws, **kw)
-        e1.record(stream)
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    ms = _timed(torch, stream, lambda: S.sdpa_fwd(q, k, v, out=o, lse=lse, workspace=ws, **kw),
+                steps, warmup, flush)
     byts = (kv_bytes                                             # K, V (+ scales)
             + 2 * wl.b * wl.h * wl.s_q * (wl.d_qk + wl.d_v)      # Q, O (bf16)
             + 4 * wl.b * wl.h * wl.s_q)                          # LSE
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"workload": wl.name, "ms": round(ms, 5), "bytes": byts,
+    return {"workload": wl.name, "ms": round(ms, 5), "bytes": byts, "timing": "median, flushed",
             "roofline": {"kernel": "fwd_decode (+ combine)", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
-def _timed(torch, stream, fn, steps, warmup):
-    """Average ms of fn() over `steps` calls, each bracketed by HIP events on
-    the launch stream, after `warmup` untimed calls."""
+def _timed(torch, stream, fn, steps, warmup, flush):
+    """Median ms of fn() over `steps` calls, each bracketed by HIP events on
+    the launch stream with the caches flushed just before (outside the
+    bracket), after `warmup` untimed calls."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     ev = []
     for _ in range(steps):
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
         e1.record(stream)
         ev.append((e0, e1))
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    return _median([a.elapsed_time(b) for a, b in ev])
 
 
-def suite_bench(S, torch, steps, warmup):
+def suite_bench(S, torch, steps, warmup, flush):
     """The other workloads of the suite (fp16 with bias and dBias; bf16 packed
     variable-length causal; bf16 causal with dropout): sdpa_fwd and the whole
     sdpa_bwd, each timed with HIP events per call.  Reported as TFLOP/s of
@@ -189,10 +216,10 @@ def suite_bench(S, torch, steps, warmup):
         o, lse, _ = S.sdpa_fwd(q, k, v, bias=bias, **kw)
         ws = torch.empty(max(1, S.bwd_workspace_size(q, k, v, **kw)), dtype=torch.uint8, device=dev)
         f_ms = _timed(torch, stream, lambda: S.sdpa_fwd(q, k, v, bias=bias, out=o, lse=lse, **kw),
-                      steps, warmup)
+                      steps, warmup, flush)
         b_ms = _timed(torch, stream, lambda: S.sdpa_bwd(q, k, v, o, do, lse, bias=bias,
                                                         want_dbias=bias is not None,
-                                                        workspace=ws, **kw), steps, warmup)
+                                                        workspace=ws, **kw), steps, warmup, flush)
         f_fl = 2.0 * pairs * (wl.d_qk + wl.d_v)
         b_fl = 2.0 * pairs * (3 * wl.d_qk + 2 * wl.d_v)
         bias_b = bias.numel() * bias.element_size() if bias is not None else 0
@@ -201,7 +228,7 @@ def suite_bench(S, torch, steps, warmup):
                 + bias_b                                                         # in
                 + (rows * wl.d_qk + rows_kv * (wl.d_qk + wl.d_v)) * e2 + bias_b)  # dQ, dK, dV, dBias
         out[str(idx)] = {
-            "workload": wl.name,
+            "workload": wl.name, "timing": "median, flushed",
             "fwd": {"ms": round(f_ms, 5), "tflops": round(f_fl / f_ms / 1e9, 2),
                     "hbm_gbs": round(f_by / f_ms / 1e6, 1), "bytes": int(f_by)},
             "bwd": {"ms": round(b_ms, 5), "tflops": round(b_fl / b_ms / 1e9, 2),
@@ -214,7 +241,7 @@ def suite_bench(S, torch, steps, warmup):
             st = torch.empty(off_st + n_st, dtype=torch.float32, device=dev)
             p_ms = _timed(torch, stream, lambda: S.sdpa_bwd_preprocess(
                 o, do, lse, cu_seqlens_q=kw["cu_seqlens_q"], max_seqlen_q=kw["max_seqlen_q"], out=st),
-                steps, warmup)
+                steps, warmup, flush)
             p_by = 2 * rows * wl.d_v * e2 + 4 * rows + 8 * rows
             out[str(idx)]["bwd_preprocess"] = {"ms": round(p_ms, 5), "bytes": int(p_by),
                                                "hbm_gbs": round(p_by / p_ms / 1e6, 1)}
@@ -223,15 +250,16 @@ def suite_bench(S, torch, steps, warmup):
     return out
 
 
-def preprocess_bench(S, torch, steps, warmup, q, o, do, lse, stats):
+def preprocess_bench(S, torch, steps, warmup, flush, q, o, do, lse, stats):
     """The standalone backward preprocess on the headline shape (HBM-bound):
     reads O, dO (io type) and LSE, writes D and LSE*log2(e) (fp32)."""
     stream = torch.cuda.current_stream()
-    ms = _timed(torch, stream, lambda: S.sdpa_bwd_preprocess(o, do, lse, out=stats), steps, warmup)
+    ms = _timed(torch, stream, lambda: S.sdpa_bwd_preprocess(o, do, lse, out=stats), steps, warmup,
+                flush)
     rows = lse.numel()
     by = 2 * o.numel() * o.element_size() + 4 * rows + 8 * rows
     gbs = by / ms / 1e6
-    return {"ms": round(ms, 5), "bytes": int(by),
+    return {"ms": round(ms, 5), "bytes": int(by), "timing": "median, flushed",
             "roofline": {"kernel": "bwd_pre", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
@@ -291,13 +319,15 @@ def main():
             print(f"bench.py: {fn.__name__} failed: {e!r}", file=sys.stderr, flush=True)
             return {"error": repr(e)}
 
+    flush = CacheFlush(torch, dev)
+    ns, nw = max(args.steps, 50), min(args.warmup, 5)  # secondary lines: medians of >= 50
     decode = {}
     if not args.no_decode:
-        decode["decode"] = extra(decode_bench, S, torch, args.steps, min(args.warmup, 10), inputs.DECODE)
-        decode["decode_int8"] = extra(decode_bench, S, torch, args.steps, min(args.warmup, 10),
-                                      inputs.DECODE_Q8)
-    ns, nw = min(args.steps, 20), min(args.warmup, 5)
-    suite = extra(suite_bench, S, torch, ns, nw) if not args.no_suite else None
+        decode["decode"] = extra(decode_bench, S, torch, ns, min(args.warmup, 10), inputs.DECODE,
+                                 flush)
+        decode["decode_int8"] = extra(decode_bench, S, torch, ns, min(args.warmup, 10),
+                                      inputs.DECODE_Q8, flush)
+    suite = extra(suite_bench, S, torch, ns, nw, flush) if not args.no_suite else None
 
     names = ("fwd", "bwd_dq", "bwd_dkdv")
     calls = (lambda: S.sdpa_fwd(q, k, v, out=o, lse=lse, **kw),
@@ -361,6 +391,14 @@ def main():
         step(names, diag)
     torch.cuda.synchronize()
     avg = averages(diag)
+    # and with the caches flushed before each step (outside the brackets):
+    # the inputs then come from HBM, not from the Infinity Cache
+    fl = {n: [] for n in names}
+    for _ in range(args.steps):
+        flush()
+        step(names, fl)
+    torch.cuda.synchronize()
+    fl_med = medians(fl)
 
     f_fl, b_fl = flops(wl)
     fwd_ms = avg["fwd"]
@@ -395,13 +433,16 @@ def main():
         "bwd": {"ms": round(bwd_ms, 5), "tflops": round(bwd_tf, 2),
                 "pct_mfma_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2),
                 "kernels_ms": {n: round(avg[n], 5) for n in ("bwd_dq", "bwd_dkdv")}},
+        "flushed_median_ms": {n: round(fl_med[n], 5) for n in names},
         "breakdown_note": "fwd/bwd ms: a diagnostic pass after the timed steps with every "
                           "kernel bracketed by HIP events; the timed steps bracket only the "
-                          "roofline kernel",
+                          "roofline kernel; flushed_median_ms: one more pass with a 512 MiB "
+                          "write before each step, medians per kernel",
         "roofline": roof,
     }
     if not args.no_suite:
-        out["bwd_preprocess"] = extra(preprocess_bench, S, torch, ns, nw, q, o, do, lse, stats)
+        out["bwd_preprocess"] = extra(preprocess_bench, S, torch, ns, nw, flush, q, o, do, lse,
+                                      stats)
         out["suite"] = suite
     if not args.no_decode:
         out.update(decode)

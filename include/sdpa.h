@@ -68,12 +68,15 @@ typedef struct {
     uint32_t struct_size;       /* must be sizeof(sdpa_problem_t) */
     sdpa_dtype_t dtype;
     int64_t b;                  /* batch; group mode: number of sequences */
-    int64_t h;                  /* heads (query and key/value heads are equal) */
+    int64_t h;                  /* query heads (key/value heads: h_kv below) */
     int64_t s_q, s_kv;          /* sequence lengths; group mode: the maxima */
     int64_t d_qk, d_v;          /* head dims of Q/K and of V/O */
     float scaling_factor;       /* multiplies Q K^T; the bias is added after it */
     int32_t is_causal;          /* top-left causal: key j visible from query i iff j <= i */
-    float dropout_probability;  /* 0 <= p < 1 */
+    /* 0 <= p <= 255/256, and p = 0 or p >= 1/512 (see the keep mask below:
+     * outside that range the 8-bit threshold would keep everything or
+     * saturate, so such p is SDPA_ERR_UNSUPPORTED). */
+    float dropout_probability;
     uint64_t dropout_seed;      /* Philox key */
     uint64_t dropout_offset;    /* Philox counter word 3 (low 32 bits used) */
     /* Optional device pointer to {seed, offset} (two uint64); when non-null
@@ -134,6 +137,11 @@ typedef struct {
     const float *k_scales, *v_scales;
     const int8_t *k_zero_points, *v_zero_points;
     sdpa_strides_t kv_scale_strides;
+    /* Group mode: rows of the packed q (>= cu_seqlens_q[b]; trailing rows
+     * past the last sequence are allowed and left alone).  softmax_lse is
+     * [h, total_q] (element (head, token) at head * total_q + token); 0
+     * means total_q = cu_seqlens_q[b].  Ignored in batch mode. */
+    int64_t total_q;
 } sdpa_problem_t;
 
 #define SDPA_KV_QUANT_NONE 0
@@ -151,7 +159,11 @@ typedef struct {
  *   byte    = (r[i & 3] >> (8 * (j & 3))) & 0xff,
  *   keep    = byte >= round(256 p);  kept values are scaled by 1/(1-p).
  * i, j are query and key positions within the sequence; in group mode b is
- * the sequence index. */
+ * the sequence index.  The kept fraction is (256 - round(256 p)) / 256,
+ * within 1/512 of 1 - p, so the expectation of a kept-and-rescaled value is
+ * off by at most (1/512) / (1 - p) relative (0.17% at p = 0.1, 2% at
+ * p = 0.9); the p outside [1/512, 255/256] that would round to "keep all"
+ * or saturate the threshold are rejected. */
 
 /* ------------------------------------------------------------------------ */
 /* Workspace.  Bytes of device scratch the caller must pass to sdpa_fwd /    */
@@ -169,8 +181,8 @@ size_t sdpa_bwd_workspace_size(const sdpa_problem_t *problem);
  *   attn_bias: nullable, [b,h,s_q,s_kv] with its own strides (batch mode
  *     only); added to the scaled scores before the softmax.
  *   softmax_lse: nullable fp32.  Batch mode: dense [b,h,s_q]; group mode:
- *     dense [h,T_q] (CK addresses LSE as head*T + token).  Null means
- *     inference: no stats are written.
+ *     dense [h,total_q] (CK addresses LSE as head*T + token; total_q as in
+ *     sdpa_problem_t).  Null means inference: no stats are written.
  *   dropout_keep_out: nullable debug output, dense uint8 [b,h,s_q,s_kv]
  *     (batch mode only): 1 where the element was kept.  Positions the causal
  *     mask hides are left unwritten.

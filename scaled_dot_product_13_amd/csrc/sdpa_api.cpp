@@ -62,6 +62,17 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
   if (!(p->dropout_probability >= 0.f && p->dropout_probability < 1.f))
     return fail(SDPA_ERR_INVALID_ARG, "dropout_probability %g outside [0, 1)",
                 (double)p->dropout_probability);
+  if (p->dropout_probability > 0.f) {
+    // the 8-bit threshold round(256 p) must be in [1, 255]: p below 1/512
+    // would keep every element (while still rescaling by 1/(1-p)), p above
+    // 255/256 would saturate the threshold
+    const double t = std::floor(256.0 * (double)p->dropout_probability + 0.5);
+    if (t < 1.0 || (double)p->dropout_probability > 255.0 / 256.0)
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "dropout_probability %g: the 8-bit keep threshold round(256 p) = %g must lie "
+                  "in [1, 255] (p in [1/512, 255/256])", (double)p->dropout_probability, t);
+  }
+  if (p->total_q < 0) return fail(SDPA_ERR_INVALID_ARG, "total_q is negative");
   if (!std::isfinite(p->scaling_factor))
     return fail(SDPA_ERR_INVALID_ARG, "scaling_factor is not finite");
   if (p->h_kv < 0 || (p->h_kv > 0 && p->h % p->h_kv != 0))
@@ -166,6 +177,7 @@ sdpa::SeqInfo seq_info(const sdpa_problem_t* p) {
   s.cu_kv = p->cu_seqlens_kv;
   s.s_q = (int32_t)p->s_q;
   s.s_kv = (int32_t)p->s_kv;
+  s.t_q = p->cu_seqlens_q ? p->total_q : 0;
   return s;
 }
 
@@ -241,18 +253,35 @@ sdpa_status_t check_kv_quant(const sdpa_problem_t* p, bool has_bias, const void*
 sdpa::DecodePlan decode_plan(const sdpa_problem_t* p) {
   return sdpa::plan_decode(p->b, p->h, kv_group(p), p->s_q, p->s_kv, decode_target_wgs());
 }
-// split-KV partials: O [ns][B H s_q][d_v] fp32, then LSE [ns][B H s_q]
+// Rows of one split-KV partial slice: the row index is the LSE index
+// (batch (b H + h) s_q + s; group h total_q + token, where every token is
+// below b s_q when total_q is not given).
+int64_t decode_rows(const sdpa_problem_t* p) {
+  if (p->cu_seqlens_q && p->total_q > 0) return p->h * p->total_q;
+  return p->b * p->h * p->s_q;
+}
+// split-KV partials: O [ns][rows][d_v] fp32, then LSE [ns][rows]
 size_t decode_part_o_bytes(const sdpa_problem_t* p, const sdpa::DecodePlan& pl) {
-  return align_up(sizeof(float) * (size_t)pl.ns * (size_t)p->b * (size_t)p->h * (size_t)p->s_q *
-                  (size_t)p->d_v);
+  return align_up(sizeof(float) * (size_t)pl.ns * (size_t)decode_rows(p) * (size_t)p->d_v);
 }
 size_t decode_workspace_bytes(const sdpa_problem_t* p, const sdpa::DecodePlan& pl) {
   if (pl.ns <= 1) return 0;
-  return decode_part_o_bytes(p, pl) +
-         align_up(sizeof(float) * (size_t)pl.ns * (size_t)p->b * (size_t)p->h * (size_t)p->s_q);
+  return decode_part_o_bytes(p, pl) + align_up(sizeof(float) * (size_t)pl.ns * (size_t)decode_rows(p));
 }
 
 }  // namespace
+
+namespace sdpa {
+bool log_enabled() { return log_on(); }
+void log_launch(const char* kernel, IoType t, int dqk, int dv, bool band, bool bias, bool drop,
+                const char* tile, dim3 grid, dim3 block) {
+  if (!log_on()) return;
+  static const char* names[] = {"f32", "f16", "bf16"};
+  std::fprintf(stderr, "[sdpa] launch %s<%s, d %d/%d, band=%d bias=%d drop=%d> tile: %s grid %u x %u x %u, "
+               "block %u\n", kernel, names[(int)t], dqk, dv, (int)band, (int)bias, (int)drop, tile,
+               grid.x, grid.y, grid.z, block.x);
+}
+}  // namespace sdpa
 
 extern "C" {
 
@@ -349,7 +378,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
     d.ns = pl.ns;
     d.chunk = pl.chunk;
     d.rg = pl.rg;
-    d.nr = p->b * p->h * p->s_q;
+    d.nr = decode_rows(p);
     if (pl.ns > 1) {
       d.part_o = (float*)workspace;
       d.part_lse = (float*)((char*)workspace + decode_part_o_bytes(p, pl));

@@ -21,6 +21,8 @@
 // reduction with no workspace, no atomics and no inter-workgroup waiting;
 // CK instead writes one fp32 dQ slice per key tile and sums the slices in
 // FmhaBwdConvertQGradKernel, and oneDNN adds fp32 dQ atomically.
+#include <type_traits>
+
 #include "sdpa_kcommon.h"
 
 // heads whose tiles are interleaved rank-major on one XCD (see xcd_work)
@@ -75,7 +77,7 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
     const int64_t base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
     a.dvec[base + row] = acc;
     if (a.lse2) {
-      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, lse_group_rows(a.seq, a.B));
       a.lse2[base + row] = a.lse[lb + row] * kLog2e;
     }
   }
@@ -583,7 +585,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
           part += to_f32<T>((uint16_t)(ov[e] >> 16)) * to_f32<T>((uint16_t)(doreg[t][e] >> 16));
         }
       }
-      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      const int64_t lb = row_stat_base(a.seq, sp, b, h, a.H, lse_group_rows(a.seq, a.B));
       lse2 = a.lse[lb + row] * kLog2e;
     }
     Drow = sum_pair32(part);
@@ -922,6 +924,8 @@ __global__ void __launch_bounds__(256) dkdv_f32(const BwdArgs a, int dqk, int dv
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
   dim3 grid((a.seq.s_q + 15) / 16, a.H, a.B), block(256);
+  log_launch("bwd_pre", t, 0, dv, false, false, false, "16 rows per workgroup, 16 lanes per row",
+             grid, block);
   if (t == IoType::BF16) hipLaunchKernelGGL(bwd_pre<__bf16>, grid, block, 0, st, a, dv);
   else if (t == IoType::F16) hipLaunchKernelGGL(bwd_pre<_Float16>, grid, block, 0, st, a, dv);
   else hipLaunchKernelGGL(bwd_pre<float>, grid, block, 0, st, a, dv);
@@ -941,7 +945,13 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
   dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H / a.G, a.B), block(512);
-#define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); return hipGetLastError(); }
+#define L(C, BI, DR)                                                                         \
+  {                                                                                          \
+    hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a);           \
+    log_launch("dkdv_mfma", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, \
+               C, BI, DR, "128 keys (8 waves, 2 roles) x 32-row query tiles, 3 LDS sets", grid, block); \
+    return hipGetLastError();                                                                \
+  }
   SDPA_FLAG_SWITCH(L)
 #undef L
   return hipErrorInvalidValue;
@@ -954,6 +964,9 @@ static hipError_t dq_dims(bool causal, bool bias, bool drop, bool pre, const Bwd
   {                                                                                         \
     if (pre) hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR, true>), grid, block, 0, st, a); \
     else hipLaunchKernelGGL((dq_mfma<T, DQK, DV, C, BI, DR, false>), grid, block, 0, st, a);    \
+    log_launch(pre ? "dq_mfma+preprocess" : "dq_mfma",                                      \
+               std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, C, BI, DR,   \
+               "128 query rows (4 waves x 32) x 64-key tiles, 2 LDS buffers", grid, block);     \
     return hipGetLastError();                                                               \
   }
   SDPA_FLAG_SWITCH(L)
@@ -983,7 +996,12 @@ hipError_t launch_bwd_dkdv(IoType t, int dqk, int dv, bool causal, const BwdArgs
   if (t == IoType::BF16) return dkdv_type<__bf16>(dqk, dv, causal, bias, drop, a, st);
   if (t == IoType::F16) return dkdv_type<_Float16>(dqk, dv, causal, bias, drop, a, st);
   dim3 grid((a.seq.s_kv + 3) / 4, a.H / a.G, a.B), block(256);
-#define L(C, BI, DR) { hipLaunchKernelGGL((dkdv_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
+#define L(C, BI, DR)                                                                   \
+  {                                                                                    \
+    hipLaunchKernelGGL((dkdv_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv);          \
+    log_launch("dkdv_f32", IoType::F32, dqk, dv, C, BI, DR, "one wave per key", grid, block); \
+    return hipGetLastError();                                                          \
+  }
   SDPA_FLAG_SWITCH(L)
 #undef L
   return hipErrorInvalidValue;
@@ -996,7 +1014,12 @@ hipError_t launch_bwd_dq(IoType t, int dqk, int dv, bool causal, const BwdArgs& 
   if (t == IoType::F16) return dq_type<_Float16>(dqk, dv, causal, bias, drop, with_pre, a, st);
   if (with_pre) return hipErrorInvalidValue;  // the fp32 path keeps the separate preprocess
   dim3 grid((a.seq.s_q + 3) / 4, a.H, a.B), block(256);
-#define L(C, BI, DR) { hipLaunchKernelGGL((dq_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv); return hipGetLastError(); }
+#define L(C, BI, DR)                                                                 \
+  {                                                                                  \
+    hipLaunchKernelGGL((dq_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv);          \
+    log_launch("dq_f32", IoType::F32, dqk, dv, C, BI, DR, "one wave per query row", grid, block); \
+    return hipGetLastError();                                                        \
+  }
   SDPA_FLAG_SWITCH(L)
 #undef L
   return hipErrorInvalidValue;

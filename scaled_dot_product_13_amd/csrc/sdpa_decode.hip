@@ -31,6 +31,7 @@
 // each lane dequantizes 16-byte chunks, x = (code - zp) * scale, into one
 // 16-bit tile per operand, and the tile step above runs unchanged on it.
 #include <algorithm>
+#include <cstdio>
 #include <type_traits>
 
 #include "sdpa_kcommon.h"
@@ -364,7 +365,7 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   }
   __syncthreads();
 
-  const int64_t st_group_rows = a.seq.cu_q ? a.seq.cu_q[a.B] : 0;
+  const int64_t st_group_rows = lse_group_rows(a.seq, a.B);
   for (int e = tid; e < 32 * DV; e += 256) {
     const int rl = e / DV, dd = e - rl * DV;
     const int rr_ = r0 + rl;
@@ -405,9 +406,10 @@ __global__ void __launch_bounds__(256) fwd_decode_combine(const FwdArgs a, const
   // (h T + token)
   T* orow;
   if (a.seq.cu_q) {
-    const int64_t T_ = a.seq.cu_q[a.B];
+    const int64_t T_ = lse_group_rows(a.seq, a.B);
     if (st >= (int64_t)a.H * T_) return;
     const int64_t h = st / T_, tok = st - h * T_;
+    if (tok >= a.seq.cu_q[a.B]) return;  // packed rows past the last sequence
     orow = (T*)a.o + h * a.so_.h + tok * a.so_.s;
   } else {
     if (st >= d.nr) return;
@@ -470,10 +472,19 @@ static hipError_t decode_dims(bool band, const FwdArgs& a, const DecodeArgs& d, 
   }
   if (qm == 0 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 0>), grid, block, 0, st, a, d);
   if (qm == 0 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 0>), grid, block, 0, st, a, d);
+  if (log_enabled()) {
+    char tile[128];
+    std::snprintf(tile, sizeof(tile), "%d row groups of 32 x %d splits of %d keys, int8 K/V %d", d.rg,
+                  d.ns, d.chunk, qm);
+    log_launch("fwd_decode", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV,
+               band, false, false, tile, grid, block);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || d.ns == 1) return e;
   dim3 cgrid((unsigned)((d.nr + 3) / 4));
   hipLaunchKernelGGL((fwd_decode_combine<T, DV>), cgrid, block, 0, st, a, d);
+  log_launch("fwd_decode_combine", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK,
+             DV, band, false, false, "one wave per row", cgrid, block);
   return hipGetLastError();
 }
 

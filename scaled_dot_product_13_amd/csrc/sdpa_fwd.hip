@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
       }
     }
     if (a.lse && g == 0) {
-      int64_t base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+      int64_t base = row_stat_base(a.seq, sp, b, h, a.H, lse_group_rows(a.seq, a.B));
       a.lse[base + row] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
     }
   }
@@ -438,7 +438,7 @@ __global__ void __launch_bounds__(256) fwd_f32(const FwdArgs a, int dqk, int dv)
     if (d < dv) og[d] = o[c] * fac;
   }
   if (a.lse && lane == 0) {
-    int64_t base = row_stat_base(a.seq, sp, b, h, a.H, a.seq.cu_q ? a.seq.cu_q[a.B] : 0);
+    int64_t base = row_stat_base(a.seq, sp, b, h, a.H, lse_group_rows(a.seq, a.B));
     a.lse[base + row] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 }
@@ -451,6 +451,8 @@ static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const Fw
 #define SDPA_FWD_CASE(C, BI, DR)                                                 \
   if (causal == C && bias == BI && drop == DR) {                                 \
     hipLaunchKernelGGL((fwd_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); \
+    log_launch("fwd_mfma", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, \
+               C, BI, DR, "128 query rows (4 waves x 32) x 64-key tiles, 2 LDS buffers", grid, block); \
     return hipGetLastError();                                                    \
   }
   SDPA_FWD_CASE(false, false, false)
@@ -486,6 +488,7 @@ hipError_t launch_fwd(IoType t, int dqk, int dv, bool causal, const FwdArgs& a, 
 #define SDPA_F32_CASE(C, BI, DR)                                                       \
   if (causal == C && bias == BI && drop == DR) {                                       \
     hipLaunchKernelGGL((fwd_f32<C, BI, DR>), grid, block, 0, st, a, dqk, dv);           \
+    log_launch("fwd_f32", IoType::F32, dqk, dv, C, BI, DR, "one wave per query row", grid, block); \
     return hipGetLastError();                                                          \
   }
   SDPA_F32_CASE(false, false, false)

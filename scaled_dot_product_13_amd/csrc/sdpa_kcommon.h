@@ -40,6 +40,13 @@ __device__ __forceinline__ T* base_ptr_mut(void* p, const Str& s, const SeqPos& 
   return (T*)p + sp.bsel * s.b + (int64_t)h * s.h + (is_q ? sp.qtok : sp.ktok) * s.s;
 }
 
+// Group mode: rows per head of the caller's LSE [h, rows] (the packed query
+// length, or cu_q[B] when the caller gave none).  0 in batch mode.
+__device__ __forceinline__ int64_t lse_group_rows(const SeqInfo& s, int B) {
+  if (!s.cu_q) return 0;
+  return s.t_q > 0 ? s.t_q : (int64_t)s.cu_q[B];
+}
+
 // Index of row 0 of (b, h) in a dense per-row fp32 array:
 //   batch mode [B,H,S_q]; group mode [H, T] with T = `group_rows`.
 __device__ __forceinline__ int64_t row_stat_base(const SeqInfo& s, const SeqPos& sp, int b,

@@ -21,6 +21,7 @@ struct SeqInfo {
   const int32_t* cu_q;   // null in batch mode
   const int32_t* cu_kv;
   int32_t s_q, s_kv;     // batch mode lengths (group mode: maxima, grid sizing only)
+  int64_t t_q;           // group mode: row count of the LSE [h, t_q]; 0 = cu_q[b]
 };
 
 struct DropoutArgs {
@@ -108,6 +109,14 @@ struct DecodePlan {
 DecodePlan plan_decode(int64_t B, int64_t H, int32_t G, int64_t s_q, int64_t s_kv,
                        int64_t target_wgs);
 constexpr int64_t kDecodeMaxSq = 16;  // thin-query path: s_q <= 16
+
+// With SDPA_LOG set in the environment: one stderr line per kernel launch
+// naming the kernel instance (io type, head dims, mask / bias / dropout
+// flags), its tile shape and its grid, as oneDNN's SDPA driver prints the
+// configuration it chose.  Host only.
+bool log_enabled();
+void log_launch(const char* kernel, IoType t, int dqk, int dv, bool band, bool bias, bool drop,
+                const char* tile, dim3 grid, dim3 block);
 
 // Launchers (each returns hipSuccess or the launch error).  `causal`,
 // `bias` and `dropout` select template instances.

@@ -52,6 +52,7 @@ class Problem(ctypes.Structure):
         ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_zero_points", ctypes.c_void_p), ("v_zero_points", ctypes.c_void_p),
         ("kv_scale_strides", Strides),
+        ("total_q", ctypes.c_int64),
     ]
 
 
@@ -137,6 +138,27 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _check_operands(q, k=None, v=None, *, quant_kv=False, cu=(), same=()):
+    """Raise TypeError unless every operand is on q's device with q's dtype
+    (k, v: int8 codes when quant_kv) and every cu_seqlens array is a
+    contiguous int32 tensor there: the library reads raw bytes, so a wrong
+    dtype would otherwise give wrong results with no error."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t is None:
+            continue
+        want = torch.int8 if quant_kv else q.dtype
+        if t.dtype != want or t.device != q.device:
+            raise TypeError(f"{name} must be {want} on {q.device}, got {t.dtype} on {t.device}")
+    for name, t in same:
+        if t is not None and (t.dtype != q.dtype or t.device != q.device):
+            raise TypeError(f"{name} must be {q.dtype} on {q.device}, got {t.dtype} on {t.device}")
+    for name, t in cu:
+        if t is not None and (t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous int32 tensor on {q.device}")
+
+
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None,
@@ -156,8 +178,11 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     fp32 [.., tokens, d / kv_group_size] laid out like k without its last
     dimension (batch [B, Hkv, S, G] or group [T, Hkv, G]); kv_zero_points
     likewise int8, or None."""
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {q.dtype}")
+    _check_operands(q, k, v, quant_kv=kv_scales is not None,
+                    cu=(("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)))
+    if seed_offset is not None and (seed_offset.dtype not in (torch.int64, torch.uint64)
+                                    or seed_offset.numel() < 2 or seed_offset.device != q.device):
+        raise TypeError("seed_offset must hold two 64-bit integers on q's device")
     group = cu_seqlens_q is not None
     p = Problem()
     p.struct_size = ctypes.sizeof(Problem)
@@ -170,6 +195,7 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
         p.d_qk, p.d_v = q.shape[2], v.shape[2]
         p.cu_seqlens_q = cu_seqlens_q.data_ptr()
         p.cu_seqlens_kv = cu_seqlens_kv.data_ptr()
+        p.total_q = q.shape[0]  # the LSE is [H, q.shape[0]]
     else:
         p.b, p.h, p.s_q, p.d_qk = q.shape
         p.s_kv, p.d_v = k.shape[2], v.shape[3]
@@ -181,22 +207,28 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     p.window_left = -1 if window_left is None else int(window_left)
     p.window_right = -1 if window_right is None else int(window_right)
     if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or alibi_slopes.stride(-1) != 1:
-            raise TypeError("alibi_slopes must be a float32 tensor with unit stride along heads")
+        if (alibi_slopes.dtype != torch.float32 or alibi_slopes.stride(-1) != 1
+                or alibi_slopes.device != q.device):
+            raise TypeError("alibi_slopes must be a float32 tensor on q's device with unit "
+                            "stride along heads")
         p.alibi_slopes = alibi_slopes.data_ptr()
         p.alibi_batch_stride = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     if kv_scales is not None:
         ks, vs = kv_scales
-        if ks.dtype != torch.float32 or vs.dtype != torch.float32 or ks.stride() != vs.stride():
-            raise TypeError("kv_scales: two float32 tensors with equal strides")
+        if (ks.dtype != torch.float32 or vs.dtype != torch.float32 or ks.stride() != vs.stride()
+                or ks.device != q.device or vs.device != q.device):
+            raise TypeError("kv_scales: two float32 tensors on q's device with equal strides")
         p.kv_quant = 1
         p.kv_group_size = int(kv_group_size)
         p.k_scales, p.v_scales = ks.data_ptr(), vs.data_ptr()
         p.kv_scale_strides = _strides(ks, group)
         if kv_zero_points is not None:
             kz, vz = kv_zero_points
-            if kz.stride() != ks.stride() or vz.stride() != ks.stride():
-                raise TypeError("kv_zero_points must have the strides of kv_scales")
+            if (kz.stride() != ks.stride() or vz.stride() != ks.stride()
+                    or kz.dtype != torch.int8 or vz.dtype != torch.int8
+                    or kz.device != q.device or vz.device != q.device):
+                raise TypeError("kv_zero_points must be int8 on q's device with the strides of "
+                                "kv_scales")
             p.k_zero_points, p.v_zero_points = kz.data_ptr(), vz.data_ptr()
     p.dropout_probability = float(dropout_p)
     p.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
@@ -222,6 +254,9 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
                      window_left=window_left, window_right=window_right,
                      alibi_slopes=alibi_slopes, kv_scales=kv_scales,
                      kv_zero_points=kv_zero_points, kv_group_size=kv_group_size)
+    _check_operands(q, same=(("bias", bias), ("out", out)))
+    if lse is not None and (lse.dtype != torch.float32 or lse.device != q.device):
+        raise TypeError("lse must be float32 on q's device")
     if out is None:
         oshape = list(q.shape)
         oshape[-1] = v.shape[-1]
@@ -256,6 +291,9 @@ def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, drop
                      max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
                      window_left=window_left, window_right=window_right,
                      alibi_slopes=alibi_slopes)
+    _check_operands(q, same=(("o", o), ("dout", dout), ("bias", bias)))
+    if lse.dtype != torch.float32 or lse.device != q.device:
+        raise TypeError("lse must be float32 on q's device")
     if dout.stride(-1) != 1:
         dout = dout.contiguous()
     dq, dk, dv = _alloc_like(q, q.shape), _alloc_like(k, k.shape), _alloc_like(v, v.shape)
@@ -295,6 +333,7 @@ def sdpa_bwd_preprocess(o, dout, lse, *, cu_seqlens_q=None, max_seqlen_q=None, o
     """Backward stats: a flat fp32 tensor holding D = rowsum(dO o O) and
     LSE*log2(e) (see stats_layout); returns it.  D alone is
     stats[:n] viewed as [B,H,S_q] (group mode [H, B*max_seqlen_q])."""
+    _check_operands(o, same=(("dout", dout),), cu=(("cu_seqlens_q", cu_seqlens_q),))
     group = cu_seqlens_q is not None
     p = Problem()
     p.struct_size = ctypes.sizeof(Problem)
@@ -304,6 +343,7 @@ def sdpa_bwd_preprocess(o, dout, lse, *, cu_seqlens_q=None, max_seqlen_q=None, o
         p.h, p.d_v = o.shape[1], o.shape[2]
         p.s_q = p.s_kv = int(max_seqlen_q)
         p.cu_seqlens_q = p.cu_seqlens_kv = cu_seqlens_q.data_ptr()
+        p.total_q = o.shape[0]
     else:
         p.b, p.h, p.s_q, p.d_v = o.shape
         p.s_kv = 1
@@ -322,6 +362,7 @@ def sdpa_bwd_dkdv(q, k, v, dout, stats, *, bias=None, dk=None, dv=None, dbias=No
     """dK, dV (and dBias) from the backward stats.  Returns (dk, dv, dbias)."""
     group = kw.get("cu_seqlens_q") is not None
     p = make_problem(q, k, v, **kw)
+    _check_operands(q, same=(("dout", dout), ("bias", bias), ("dbias", dbias)))
     dk = _alloc_like(k, k.shape) if dk is None else dk
     dv = _alloc_like(v, v.shape) if dv is None else dv
     if want_dbias and bias is not None and dbias is None:
@@ -339,6 +380,7 @@ def sdpa_bwd_dq_preprocess(q, k, v, o, dout, lse, *, bias=None, dq=None, stats=N
     Returns (dq, stats); run sdpa_bwd_dkdv on the stats afterwards."""
     group = kw.get("cu_seqlens_q") is not None
     p = make_problem(q, k, v, **kw)
+    _check_operands(q, same=(("o", o), ("dout", dout), ("bias", bias), ("dq", dq)))
     dq = _alloc_like(q, q.shape) if dq is None else dq
     n, off = stats_layout(p.b, p.h, p.s_q)
     if stats is None:
@@ -356,6 +398,7 @@ def sdpa_bwd_dq(q, k, v, dout, stats, *, bias=None, dq=None, **kw):
     """dQ from the backward stats.  Returns dq."""
     group = kw.get("cu_seqlens_q") is not None
     p = make_problem(q, k, v, **kw)
+    _check_operands(q, same=(("dout", dout), ("bias", bias), ("dq", dq)))
     dq = _alloc_like(q, q.shape) if dq is None else dq
     _check(_lib.sdpa_bwd_dq(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k), _strides(k, group),
                             _ptr(v), _strides(v, group), _ptr(bias), _strides(bias, False),

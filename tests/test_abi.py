@@ -175,3 +175,48 @@ def test_backward_workspace_rules(S):
     assert S.lib().sdpa_fwd_workspace_size(ctypes.byref(p)) == 0
     # an invalid problem sizes to zero
     assert S.lib().sdpa_bwd_workspace_size(ctypes.byref(_problem(S, d_qk=96, d_v=96))) == 0
+
+
+def test_dropout_probability_range(S):
+    # the 8-bit threshold round(256 p) must lie in [1, 255]
+    L = S.lib()
+    for p in (1.0 / 1024, 0.0019, 0.999, 255.5 / 256):
+        assert _fwd(S, _problem(S, p=p)) == S.SDPA_ERR_UNSUPPORTED, p
+        assert b"threshold" in L.sdpa_last_error_message()
+        assert _bwd(S, _problem(S, p=p)) == S.SDPA_ERR_UNSUPPORTED, p
+    # the end points of the range pass validation (they then reach the fake
+    # pointers' alignment checks, not the probability check)
+    for p in (1.0 / 512, 0.1, 255.0 / 256):
+        _fwd(S, _problem(S, p=p), q=FAKE + 2)
+        assert b"threshold" not in L.sdpa_last_error_message(), p
+    p = _problem(S, cu_q=FAKE, cu_kv=FAKE)
+    p.total_q = -1
+    assert _fwd(S, p) == S.SDPA_ERR_INVALID_ARG
+    assert b"total_q" in L.sdpa_last_error_message()
+
+
+def test_binding_rejects_mismatched_operands(S):
+    # the library reads raw bytes, so the binding refuses operands whose dtype
+    # or device differs from q's, and cu_seqlens that are not int32
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="k must be"):
+        S.make_problem(q, k.float(), k)
+    with pytest.raises(TypeError, match="v must be"):
+        S.make_problem(q, k, k.half())
+    with pytest.raises(TypeError, match="unsupported dtype"):
+        S.make_problem(q.to(torch.float64), k, k)
+    qg = torch.zeros(40, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 16, 40], dtype=torch.int64)
+    with pytest.raises(TypeError, match="cu_seqlens_q"):
+        S.make_problem(qg, qg, qg, cu_seqlens_q=cu, cu_seqlens_kv=cu.int(), max_seqlen_q=24,
+                       max_seqlen_kv=24)
+    # group mode: the LSE row stride is the packed length of q
+    p = S.make_problem(qg, qg, qg, cu_seqlens_q=cu.int(), cu_seqlens_kv=cu.int(), max_seqlen_q=24,
+                       max_seqlen_kv=24)
+    assert p.total_q == 40
+    with pytest.raises(TypeError, match="bias must be"):
+        S.sdpa_fwd(q, k, k, bias=torch.zeros(1, 2, 16, 16, dtype=torch.float32))
+    with pytest.raises(TypeError, match="dout must be"):
+        S.sdpa_bwd(q, k, k, q, q.float(), torch.zeros(1, 2, 16))

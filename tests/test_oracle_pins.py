@@ -88,6 +88,29 @@ def test_drop_threshold_values():
     assert O.drop_threshold(0.999) == 255
 
 
+def test_keep_bit_layout_reproduces_known_answer_bytes():
+    """The keep decision's position-to-byte mapping, pinned bit for bit to
+    the Random123 known-answer vectors.  Each KAT counter (c0, c1, c2, c3)
+    and key (k0, k1) is read as key position j = 4 c0 + (j & 3), query
+    position i = 4 c1 + (i & 3), head index b*H + h = c2, offset = c3 and
+    seed = k0 + 2^32 k1.  For every (i & 3, j & 3) the random byte is
+    recovered by sweeping the drop threshold t = round(256 p) over 0..255
+    (p = t / 256): the element is kept iff byte >= t, so the byte is the
+    largest t that still keeps it.  It must equal byte (j & 3) of output
+    word (i & 3).  Swapping i and j, or the word and byte indices, fails."""
+    for ctr, key, want in _kat():
+        seed = key[0] | (key[1] << 32)
+        for ii in range(4):
+            for jj in range(4):
+                i, j = 4 * ctr[1] + ii, 4 * ctr[0] + jj
+                kept = [O.keep_bit(seed, ctr[3], ctr[2], i, j, t / 256.0) for t in range(256)]
+                assert kept[0] == 1
+                byte = max(t for t in range(256) if kept[t])
+                # monotone: kept exactly for t <= byte
+                assert kept == [1] * (byte + 1) + [0] * (255 - byte)
+                assert byte == (want[ii] >> (8 * jj)) & 0xFF, (ctr, ii, jj)
+
+
 def test_keep_mask_statistics_and_sensitivity():
     B, H, S = 1, 2, 256
     q = _rand((B, H, S, 16), 1)
@@ -577,6 +600,12 @@ MUTANTS = {
     "rescale": ("double rescale = 1.0 / (1.0 - (double)h->p_drop);", "double rescale = 1.0;"),
     # a wrong Philox word order
     "philox": ("uint32_t n1 = lo1;", "uint32_t n1 = lo0;"),
+    # the keep counter with query and key positions swapped
+    "keep_counter": ("uint32_t ctr[4] = {(uint32_t)(j >> 2), (uint32_t)(i >> 2), bh,",
+                     "uint32_t ctr[4] = {(uint32_t)(i >> 2), (uint32_t)(j >> 2), bh,"),
+    # the keep byte taken with word and byte indices swapped
+    "keep_byte": ("uint32_t byte = (r[i & 3] >> (8 * (j & 3))) & 0xffu;",
+                  "uint32_t byte = (r[j & 3] >> (8 * (i & 3))) & 0xffu;"),
     # ALiBi with the wrong sign, without the absolute value, or misaligned
     "alibi_sign": ("s[j] -= h->alibi_slope", "s[j] += h->alibi_slope"),
     "alibi_abs": ("fabs((double)(j - i - h->alibi_off))", "((double)(j - i - h->alibi_off))"),
