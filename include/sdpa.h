@@ -293,6 +293,36 @@ sdpa_status_t sdpa_bwd_dq_preprocess(const sdpa_problem_t *problem,
                                      void *dq, sdpa_strides_t dq_strides,
                                      void *stream);
 
+/* Backward with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * kernels and results as sdpa_bwd: the outputs are bitwise those of sdpa_bwd
+ * on the same inputs.  The backward stats (D and LSE*log2(e), the workspace
+ * of sdpa_bwd) live in a device array of the library instead:
+ * 2 * SDPA_NOALLOC_MAX_ROWS floats (8 MiB) on each GPU the library runs on,
+ * held until the process ends.  It calls no allocating routine.
+ *   - b*h*s_q must not exceed SDPA_NOALLOC_MAX_ROWS, else SDPA_ERR_WORKSPACE
+ *     (group mode counts b*h*s_q with s_q the maximum length);
+ *   - calls that overlap on one GPU (several streams or threads) share the
+ *     array and race: the caller serialises them.  The array needs no
+ *     clearing: every element a call reads was written earlier in that call.
+ * Errors as for sdpa_bwd; SDPA_ERR_HIP if the array's device address cannot
+ * be obtained. */
+#define SDPA_NOALLOC_MAX_ROWS (1 << 20)
+sdpa_status_t sdpa_bwd_noalloc(const sdpa_problem_t *problem,
+                               const void *q, sdpa_strides_t q_strides,
+                               const void *k, sdpa_strides_t k_strides,
+                               const void *v, sdpa_strides_t v_strides,
+                               const void *attn_bias, sdpa_strides_t bias_strides,
+                               const void *o, sdpa_strides_t o_strides,
+                               const void *d_o, sdpa_strides_t do_strides,
+                               const float *softmax_lse,
+                               void *dq, sdpa_strides_t dq_strides,
+                               void *dk, sdpa_strides_t dk_strides,
+                               void *dv, sdpa_strides_t dv_strides,
+                               void *dbias, sdpa_strides_t dbias_strides,
+                               void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sdpa_status_string(sdpa_status_t status);
 

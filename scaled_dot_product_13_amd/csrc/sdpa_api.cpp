@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -269,6 +270,38 @@ size_t decode_workspace_bytes(const sdpa_problem_t* p, const sdpa::DecodePlan& p
   return decode_part_o_bytes(p, pl) + align_up(sizeof(float) * (size_t)pl.ns * (size_t)decode_rows(p));
 }
 
+// ---- the no-allocation backward's stats array -------------------------------
+// File-scope device memory, one copy per GPU: D then LSE*log2(e), each
+// SDPA_NOALLOC_MAX_ROWS floats (the layout of the backward workspace for
+// any problem within the limit: stats_half_bytes(p) <= 4 * MAX_ROWS).  Host
+// code never uses the name `scratch` itself (on the host it is a stand-in,
+// not a device address): its per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kNoAllocRows = SDPA_NOALLOC_MAX_ROWS;
+__device__ __attribute__((aligned(256))) float scratch[2 * kNoAllocRows];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+sdpa_status_t noalloc_stats(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SDPA_ERR_UNSUPPORTED, "device %d beyond the %d devices the library tracks", dev,
+                kMaxDevices);
+  void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SDPA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev].store(ptr, std::memory_order_release);  // same value if two threads race
+  }
+  *out = ptr;
+  return SDPA_OK;
+}
+
 }  // namespace
 
 namespace sdpa {
@@ -508,6 +541,30 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   }
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return SDPA_OK;
+}
+
+sdpa_status_t sdpa_bwd_noalloc(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_s,
+                               const void* k, sdpa_strides_t k_s, const void* v,
+                               sdpa_strides_t v_s, const void* attn_bias, sdpa_strides_t bias_s,
+                               const void* o, sdpa_strides_t o_s, const void* d_o,
+                               sdpa_strides_t do_s, const float* softmax_lse, void* dq,
+                               sdpa_strides_t dq_s, void* dk, sdpa_strides_t dk_s, void* dv,
+                               sdpa_strides_t dv_s, void* dbias, sdpa_strides_t dbias_s,
+                               void* stream) {
+  g_msg[0] = 0;
+  sdpa_status_t st = check_problem(p);
+  if (st != SDPA_OK) return st;
+  if (empty_problem(p)) return SDPA_OK;
+  const int64_t rows = p->b * p->h * p->s_q;
+  if (rows > kNoAllocRows)
+    return fail(SDPA_ERR_WORKSPACE, "b*h*s_q = %lld exceeds the no-allocation limit of %lld rows",
+                (long long)rows, (long long)kNoAllocRows);
+  void* ws = nullptr;
+  if ((st = noalloc_stats(&ws)) != SDPA_OK) return st;
+  // the stats layout inside the array is the workspace layout of sdpa_bwd
+  return sdpa_bwd(p, q, q_s, k, k_s, v, v_s, attn_bias, bias_s, o, o_s, d_o, do_s, softmax_lse,
+                  dq, dq_s, dk, dk_s, dv, dv_s, dbias, dbias_s, ws,
+                  sizeof(float) * 2 * (size_t)kNoAllocRows, stream);
 }
 
 // Shared checks of the operands the dK/dV and dQ kernels read.

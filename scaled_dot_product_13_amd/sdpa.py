@@ -74,6 +74,10 @@ _lib.sdpa_bwd.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Str
                           _vp, Strides, _vp, Strides, _vp, _vp, Strides, _vp, Strides,
                           _vp, Strides, _vp, Strides, _vp, _sz, _vp]
 _lib.sdpa_bwd.restype = ctypes.c_int
+_lib.sdpa_bwd_noalloc.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
+                                  _vp, Strides, _vp, Strides, _vp, _vp, Strides, _vp, Strides,
+                                  _vp, Strides, _vp, Strides, _vp]
+_lib.sdpa_bwd_noalloc.restype = ctypes.c_int
 _lib.sdpa_bwd_preprocess.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, _vp, _vp]
 _lib.sdpa_bwd_preprocess.restype = ctypes.c_int
 _lib.sdpa_bwd_dkdv.argtypes = [_P, _vp, Strides, _vp, Strides, _vp, Strides, _vp, Strides,
@@ -307,6 +311,37 @@ def sdpa_bwd(q, k, v, o, dout, lse, *, bias=None, scale=None, causal=False, drop
                          _ptr(dq), _strides(dq, group), _ptr(dk), _strides(dk, group),
                          _ptr(dv), _strides(dv, group), _ptr(dbias), _strides(dbias, False),
                          _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, dbias
+
+
+NOALLOC_MAX_ROWS = 1 << 20  # SDPA_NOALLOC_MAX_ROWS
+
+
+def sdpa_bwd_noalloc(q, k, v, o, dout, lse, *, bias=None, dq=None, dk=None, dv=None, dbias=None,
+                     want_dbias=False, **kw):
+    """Backward through sdpa_bwd_noalloc: no workspace, the library's own
+    per-GPU stats array instead (b*h*s_q <= NOALLOC_MAX_ROWS; calls on one
+    GPU must not overlap).  Pass preallocated dq, dk, dv (and dbias) for a
+    call that allocates nothing.  Returns (dq, dk, dv, dbias or None)."""
+    group = kw.get("cu_seqlens_q") is not None
+    p = make_problem(q, k, v, **kw)
+    _check_operands(q, same=(("o", o), ("dout", dout), ("bias", bias), ("dq", dq), ("dk", dk),
+                             ("dv", dv), ("dbias", dbias)))
+    if lse.dtype != torch.float32 or lse.device != q.device:
+        raise TypeError("lse must be float32 on q's device")
+    if dout.stride(-1) != 1:
+        raise TypeError("dout must have unit stride in its last dimension")
+    dq = _alloc_like(q, q.shape) if dq is None else dq
+    dk = _alloc_like(k, k.shape) if dk is None else dk
+    dv = _alloc_like(v, v.shape) if dv is None else dv
+    if want_dbias and bias is not None and dbias is None:
+        dbias = _alloc_like(bias, bias.shape)
+    _check(_lib.sdpa_bwd_noalloc(ctypes.byref(p), _ptr(q), _strides(q, group), _ptr(k),
+                                 _strides(k, group), _ptr(v), _strides(v, group), _ptr(bias),
+                                 _strides(bias, False), _ptr(o), _strides(o, group), _ptr(dout),
+                                 _strides(dout, group), _ptr(lse), _ptr(dq), _strides(dq, group),
+                                 _ptr(dk), _strides(dk, group), _ptr(dv), _strides(dv, group),
+                                 _ptr(dbias), _strides(dbias, False), _stream()))
     return dq, dk, dv, dbias
 
 
