@@ -215,6 +215,21 @@ def _alibi(alibi_slopes, n_batch, n_heads, causal, bottom_right, window_left, wi
     return sl, (bottom_right or not masked)
 
 
+def unpack_int4(packed, signed):
+    """4-bit codes from bytes holding two codes each: code 2i of a row is the
+    low nibble of byte i, code 2i + 1 its high nibble (the low-nibble-first
+    packing of sub-byte data types in oneDNN's memory descriptors, which the
+    micro SDPA host driver accepts for key / value quantization).  Signed
+    codes are 4-bit two's complement (-8 .. 7), unsigned codes 0 .. 15.
+    packed uint8 [..., D / 2] -> int64 [..., D]."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    lo, hi = b & 0xF, (b >> 4) & 0xF
+    codes = np.stack([lo, hi], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    if signed:
+        codes = np.where(codes >= 8, codes - 16, codes)
+    return codes
+
+
 def dequantize_kv(codes, scales, group_size, zero_points=None):
     """K or V from 8-bit integer codes with one scale (and optionally one
     integer zero point) per token and per group of `group_size` consecutive

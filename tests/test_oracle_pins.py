@@ -557,6 +557,52 @@ def test_dequantize_zero_point_shift_and_identity():
     assert O.dequantize_kv(one, g, 16)[0, 0, 17] == 3.0
 
 
+def _pack_nibbles_by_arithmetic(codes):
+    """Test-side packer, written with integer arithmetic rather than bit
+    operations: byte i = (code 2i mod 16) + 16 (code 2i+1 mod 16)."""
+    c = np.asarray(codes, dtype=np.int64) % 16
+    return (c[..., 0::2] + 16 * c[..., 1::2]).astype(np.uint8)
+
+
+@pytest.mark.parametrize("signed", [True, False])
+def test_unpack_int4_inverts_the_packing(signed):
+    # every code value in every position, packed by a different method
+    rng = np.random.default_rng(271 + signed)
+    lo, hi = (-8, 8) if signed else (0, 16)
+    codes = rng.integers(lo, hi, size=(3, 5, 128))
+    codes[0, 0, :16] = np.arange(lo, hi)
+    codes[0, 1, 1:17:2] = np.arange(lo, hi)[:8]
+    assert np.array_equal(O.unpack_int4(_pack_nibbles_by_arithmetic(codes), signed), codes)
+
+
+def test_unpack_int4_byte_table():
+    # all 256 bytes: the low nibble is the even code, the high nibble the odd
+    # one; signed codes are 4-bit two's complement
+    b = np.arange(256, dtype=np.uint8)[None, :]
+    u = O.unpack_int4(b, False)[0]
+    s = O.unpack_int4(b, True)[0]
+    for v in range(256):
+        assert (u[2 * v], u[2 * v + 1]) == (v % 16, v // 16)
+        assert (s[2 * v] - u[2 * v]) % 16 == 0 and -8 <= s[2 * v] <= 7
+        assert (s[2 * v + 1] - u[2 * v + 1]) % 16 == 0 and -8 <= s[2 * v + 1] <= 7
+    assert s[2 * 0x8F] == -1 and s[2 * 0x8F + 1] == -8 and s[2 * 0x07] == 7
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_int4_dequantize_is_within_half_a_step(group):
+    # a test-side symmetric 4-bit quantizer (scale = max|x| / 7, codes in
+    # -7 .. 7), packed, unpacked by the oracle and dequantized: within half a
+    # step of the data
+    x = _rand((2, 3, 40, 128), 281)
+    xg = x.reshape(2, 3, 40, 128 // group, group)
+    scale = np.abs(xg).max(-1) / 7.0
+    codes = np.clip(np.rint(xg / scale[..., None]), -7, 7).astype(np.int64).reshape(x.shape)
+    xr = O.dequantize_kv(O.unpack_int4(_pack_nibbles_by_arithmetic(codes), True), scale, group)
+    bound = np.repeat(scale, group, axis=-1) / 2
+    assert np.all(np.abs(xr - x) <= bound * (1 + 1e-12))
+    assert np.max(np.abs(xr - x) / bound) > 0.9
+
+
 # ------------------------------------------------------------ group mode ----
 def test_group_mode_equals_batch_mode_per_sequence():
     H, D = 2, 6
