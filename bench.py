@@ -14,9 +14,9 @@ The line also carries a "decode" object: the thin-query forward (split-KV)
 on the decode workload (bf16, B=16, 32 query heads over 8 key/value heads,
 one query row per sequence, S_kv=8192, d=128), timed the same way and
 reported as algorithmic HBM bytes (K, V, Q, O, LSE) per second against the
-8 TB/s peak; and "decode_int8": the same step over an int8 K/V cache with
-fp32 scales per token and group of 32 head-dim elements (bytes: codes,
-scales, Q, O, LSE).
+8 TB/s peak; "decode_int8": the same step over an int8 K/V cache with fp32
+scales per token and group of 32 head-dim elements (bytes: codes, scales,
+Q, O, LSE); and "decode_int4": over signed 4-bit codes, two per byte.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-suite]
 """
@@ -137,10 +137,13 @@ def decode_bench(S, torch, steps, warmup, wl, flush):
     hk = wl.h_kv or wl.h
     kv_elems = wl.b * hk * wl.s_kv * (wl.d_qk + wl.d_v)
     if wl.kv_quant is not None:
-        gs, with_zp = wl.kv_quant
+        gs, with_zp = wl.kv_quant[:2]
+        fmt = wl.kv_quant[2] if len(wl.kv_quant) > 2 else "s8"
         kw.update(kv_scales=(x["k_scales"].to(dev), x["v_scales"].to(dev)), kv_group_size=gs,
-                  kv_zero_points=(x["k_zp"].to(dev), x["v_zp"].to(dev)) if with_zp else None)
-        kv_bytes = kv_elems + kv_elems // gs * (4 + (1 if with_zp else 0))
+                  kv_zero_points=(x["k_zp"].to(dev), x["v_zp"].to(dev)) if with_zp else None,
+                  kv_format=fmt)
+        code_bytes = kv_elems if fmt == "s8" else kv_elems // 2
+        kv_bytes = code_bytes + kv_elems // gs * (4 + (1 if with_zp else 0))
     else:
         kv_bytes = 2 * kv_elems
     del x
@@ -327,6 +330,8 @@ def main():
                                  flush)
         decode["decode_int8"] = extra(decode_bench, S, torch, ns, min(args.warmup, 10),
                                       inputs.DECODE_Q8, flush)
+        decode["decode_int4"] = extra(decode_bench, S, torch, ns, min(args.warmup, 10),
+                                      inputs.DECODE_Q4, flush)
     suite = extra(suite_bench, S, torch, ns, nw, flush) if not args.no_suite else None
 
     names = ("fwd", "bwd_dq", "bwd_dkdv")

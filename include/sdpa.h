@@ -122,16 +122,22 @@ typedef struct {
     const float *alibi_slopes;
     int64_t alibi_batch_stride;
     /* Quantized K/V for the thin-query forward (the oneDNN micro SDPA host
-     * driver's grouped key / value scales and zero points).  With
-     * kv_quant = SDPA_KV_QUANT_S8, k and v hold int8 codes (their strides
-     * count bytes) and
-     *   K[t][c] = (k[t][c] - k_zero_points[t][c/g]) * k_scales[t][c/g]
+     * driver's grouped key / value scales and zero points).  k and v hold
+     * integer codes (their strides count bytes):
+     *   SDPA_KV_QUANT_S8  int8 codes, one per byte;
+     *   SDPA_KV_QUANT_S4  signed 4-bit codes (-8 .. 7, two's complement),
+     *   SDPA_KV_QUANT_U4  unsigned 4-bit codes (0 .. 15): two per byte, code
+     *                     2i of a row in the low nibble of byte i and code
+     *                     2i + 1 in its high nibble (rows of d/2 bytes);
+     * and
+     *   K[t][c] = (code[t][c] - k_zero_points[t][c/g]) * k_scales[t][c/g]
      * (V likewise), g = kv_group_size, t a token of one (batch, K/V head).
      * Scales are fp32 and zero points int8 (nullable together: then 0), all
      * four at kv_scale_strides (elements; the group index is contiguous).
      * Supported by sdpa_fwd only, for thin-query problems (16-bit q and o,
      * s_q <= 16, d_qk = d_v = 128, no bias, ALiBi or dropout) with g in
-     * {16, 32, 64, 128}; int8 rows must be 16-byte aligned. */
+     * {16, 32, 64, 128} for int8 and {32, 64, 128} for 4-bit codes; code
+     * rows must be 16-byte aligned. */
     int32_t kv_quant;
     int32_t kv_group_size;
     const float *k_scales, *v_scales;
@@ -146,6 +152,8 @@ typedef struct {
 
 #define SDPA_KV_QUANT_NONE 0
 #define SDPA_KV_QUANT_S8 1
+#define SDPA_KV_QUANT_S4 2
+#define SDPA_KV_QUANT_U4 3
 
 #define SDPA_MASK_BOTTOM_RIGHT 1u
 #define SDPA_MASK_WINDOW 2u

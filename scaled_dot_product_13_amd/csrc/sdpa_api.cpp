@@ -83,7 +83,8 @@ sdpa_status_t check_problem(const sdpa_problem_t* p) {
     return fail(SDPA_ERR_INVALID_ARG, "unknown mask_flags bits 0x%x", p->mask_flags);
   if (p->alibi_slopes && p->alibi_batch_stride < 0)
     return fail(SDPA_ERR_INVALID_ARG, "alibi_batch_stride is negative");
-  if (p->kv_quant != SDPA_KV_QUANT_NONE && p->kv_quant != SDPA_KV_QUANT_S8)
+  if (p->kv_quant != SDPA_KV_QUANT_NONE && p->kv_quant != SDPA_KV_QUANT_S8 &&
+      p->kv_quant != SDPA_KV_QUANT_S4 && p->kv_quant != SDPA_KV_QUANT_U4)
     return fail(SDPA_ERR_INVALID_ARG, "unknown kv_quant %d", p->kv_quant);
   if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_kv == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must both be set or both null");
@@ -221,19 +222,20 @@ int64_t decode_target_wgs() {
   }();
   return n;
 }
-// int8 K/V: everything the thin-query kernel's int8 mode assumes.
+// Quantized K/V: everything the thin-query kernel's quantized modes assume.
 sdpa_status_t check_kv_quant(const sdpa_problem_t* p, bool has_bias, const void* k,
                              sdpa_strides_t k_s, const void* v, sdpa_strides_t v_s) {
   if (p->dtype == SDPA_F32 || has_bias || p->dropout_probability > 0.f || p->s_q > sdpa::kDecodeMaxSq)
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs a thin-query forward: 16-bit q, s_q <= %lld, "
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V needs a thin-query forward: 16-bit q, s_q <= %lld, "
                 "no bias, ALiBi or dropout", (long long)sdpa::kDecodeMaxSq);
   if (!decode_eligible(p, false))
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs the thin-query kernel (SDPA_DECODE=0 is set)");
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V needs the thin-query kernel (SDPA_DECODE=0 is set)");
   if (p->d_qk != 128 || p->d_v != 128)
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V needs d_qk = d_v = 128");
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V needs d_qk = d_v = 128");
   const int g = p->kv_group_size;
-  if (!(g == 16 || g == 32 || g == 64 || g == 128))
-    return fail(SDPA_ERR_UNSUPPORTED, "kv_group_size %d not in {16, 32, 64, 128}", g);
+  const bool four = p->kv_quant != SDPA_KV_QUANT_S8;
+  if (!(g == 32 || g == 64 || g == 128 || (g == 16 && !four)))
+    return fail(SDPA_ERR_UNSUPPORTED, "kv_group_size %d not in {%s32, 64, 128}", g, four ? "" : "16, ");
   if (!p->k_scales || !p->v_scales) return fail(SDPA_ERR_INVALID_ARG, "k_scales / v_scales are null");
   if ((p->k_zero_points == nullptr) != (p->v_zero_points == nullptr))
     return fail(SDPA_ERR_INVALID_ARG, "k_zero_points and v_zero_points must both be set or both null");
@@ -245,7 +247,7 @@ sdpa_status_t check_kv_quant(const sdpa_problem_t* p, bool has_bias, const void*
     const void* t = i ? v : k;
     const sdpa_strides_t s = i ? v_s : k_s;
     if ((uintptr_t)t % 16 || s.head % 16 || s.seq % 16 || (!group && s.batch % 16))
-      return fail(SDPA_ERR_UNSUPPORTED, "int8 %s: base and strides must be multiples of 16 bytes",
+      return fail(SDPA_ERR_UNSUPPORTED, "quantized %s: base and strides must be multiples of 16 bytes",
                   i ? "v" : "k");
   }
   return SDPA_OK;
@@ -354,7 +356,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   if (empty_problem(p)) return SDPA_OK;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
-  const bool q8 = p->kv_quant == SDPA_KV_QUANT_S8;
+  const bool q8 = p->kv_quant != SDPA_KV_QUANT_NONE;  // quantized K/V codes
   if ((st = check_tensor(p, k, k_s, "k", vec && !q8)) != SDPA_OK) return st;
   if ((st = check_tensor(p, v, v_s, "v", vec && !q8)) != SDPA_OK) return st;
   if ((st = check_tensor(p, o, o_s, "o", vec)) != SDPA_OK) return st;
@@ -407,6 +409,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
       d.v_zp = p->v_zero_points;
       d.ss = to_str(p->kv_scale_strides);
       d.qgs = p->kv_group_size;
+      d.qfmt = p->kv_quant == SDPA_KV_QUANT_S8 ? 1 : p->kv_quant == SDPA_KV_QUANT_S4 ? 2 : 3;
     }
     d.ns = pl.ns;
     d.chunk = pl.chunk;
@@ -447,7 +450,7 @@ sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t* p, const void* o, sdpa_s
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
   if (p->kv_quant != SDPA_KV_QUANT_NONE)
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V is a forward (inference) feature only");
   if (empty_problem(p)) return SDPA_OK;
   if ((st = check_tensor(p, o, o_s, "o", true)) != SDPA_OK) return st;
   if ((st = check_tensor(p, d_o, do_s, "d_o", true)) != SDPA_OK) return st;
@@ -478,7 +481,7 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   sdpa_status_t st = check_problem(p);
   if (st != SDPA_OK) return st;
   if (p->kv_quant != SDPA_KV_QUANT_NONE)
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V is a forward (inference) feature only");
   if (empty_problem(p)) return SDPA_OK;
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
@@ -575,7 +578,7 @@ static sdpa_status_t check_bwd_inputs(const sdpa_problem_t* p, const void* q, sd
                                       const float* stats) {
   sdpa_status_t st;
   if (p->kv_quant != SDPA_KV_QUANT_NONE)
-    return fail(SDPA_ERR_UNSUPPORTED, "int8 K/V is a forward (inference) feature only");
+    return fail(SDPA_ERR_UNSUPPORTED, "quantized K/V is a forward (inference) feature only");
   const bool vec = p->dtype != SDPA_F32;
   if ((st = check_tensor(p, q, q_s, "q", vec)) != SDPA_OK) return st;
   if ((st = check_tensor(p, k, k_s, "k", vec)) != SDPA_OK) return st;

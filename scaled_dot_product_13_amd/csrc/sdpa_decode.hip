@@ -69,11 +69,89 @@ __device__ __forceinline__ void dequant_tile(const uint16_t* src, T* dst, const 
   }
 }
 
-// QM: 0 = 16-bit K/V, 1 = int8 K/V with scales, 2 = int8 K/V with scales
-// and zero points
+// A 32-row tile of 4-bit codes (rows of D/2 bytes, two codes per byte, low
+// nibble first), staged row-major without swizzle, dequantized into a
+// 16-bit tile (Lds<D> layout).  Lane l converts 16-byte chunk l % (D/32)
+// (32 codes) of rows l / (D/32) + (64 / (D/32)) u, u = 0, 1; sc[u] / zp[u]
+// are that chunk's scale and zero point (one group per chunk: g >= 32).
+template <typename T, int D, bool SIGNED>
+__device__ __forceinline__ void dequant_tile4(const uint8_t* src, T* dst, const float (&sc)[4],
+                                              const int (&zp)[4], int lane) {
+  constexpr int LPR = D / 32;  // lanes (16-byte chunks) per row
+  constexpr int RSTEP = 64 / LPR;
+  const int cc = lane % LPR;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = lane / LPR + RSTEP * u;
+    const u32x4 raw = lds_load16(lds_addr(src + (D / 2) * row + 16 * cc));
+    const float s = sc[u], o = -(float)zp[u] * sc[u];
+    uint32_t outw[16];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint32_t x = raw[wd];
+      float f[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int code = SIGNED ? ((int)(x << (28 - 4 * k)) >> 28) : (int)((x >> (4 * k)) & 15u);
+        f[k] = __builtin_fmaf((float)code, s, o);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) outw[4 * wd + k] = pack2<T>(f[2 * k], f[2 * k + 1]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(u32x4*)(dst + Lds<D>::off(row, 32 * cc + 8 * q)) =
+          u32x4{outw[4 * q], outw[4 * q + 1], outw[4 * q + 2], outw[4 * q + 3]};
+  }
+}
+
+// Direct-to-LDS loads of a 32-row tile of 4-bit codes (rows of D/2 bytes)
+// into a row-major, unswizzled staging tile: 16-byte chunk c of the tile is
+// row c / (D/32), column chunk c % (D/32), at LDS byte 16 c; with one wave,
+// lane l loads chunks l + 64 j.  Rows past row_limit are clamped (masked by
+// the caller), as in TileLoader.
+template <int D> struct Int4TileLoader {
+  static constexpr int CPR = D / 32;  // 16-byte chunks per row
+  static constexpr int PER_WAVE = 32 * CPR / 64;
+  static_assert(32 * CPR % 64 == 0, "whole wave loads");
+  const char* g;
+  int64_t stride_b;
+  uint32_t voff[PER_WAVE];
+  __device__ __forceinline__ void init(const void* g_, int64_t row_stride_bytes, int, int lane) {
+    g = (const char*)g_;
+    stride_b = row_stride_bytes;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int c = 64 * j + lane;
+      voff[j] = (uint32_t)((c / CPR) * stride_b + 16 * (c % CPR));
+    }
+  }
+  __device__ __forceinline__ void load(void* tile, int row0, int row_limit, int, int lane) const {
+    if (row0 + 32 <= row_limit) {
+      const char* base = g + row0 * stride_b;
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(base + voff[j]),
+                                         (lds_void*)((char*)tile + 1024 * j), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int c = 64 * j + lane;
+        const int gr = min(row0 + c / CPR, row_limit - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(g + gr * stride_b + 16 * (c % CPR)),
+                                         (lds_void*)((char*)tile + 1024 * j), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// QM: 0 = 16-bit K/V; quantized K/V with scales: 1 = int8, 3 = signed
+// 4-bit, 5 = unsigned 4-bit; 2, 4, 6: the same with zero points
 template <typename T, int DQK, int DV, bool BAND, int QM>
 __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const DecodeArgs d) {
-  constexpr bool Q8 = QM != 0;
+  constexpr bool Q8 = QM != 0;     // quantized K/V (8- or 4-bit codes)
+  constexpr bool Q4 = QM >= 3;     // 4-bit codes
+  constexpr bool QZP = QM == 2 || QM == 4 || QM == 6;
   constexpr int BC = 32;        // keys per wave tile
   constexpr int KT = DQK / 16;  // 16-wide k-steps over d_qk
   constexpr int DB = DV / 32;   // 32-wide blocks of d_v
@@ -85,7 +163,7 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   // K and V tile (sK0, sV0) and double-buffered int8 staging tiles.  After
   // the loop, the wave's partial O (32 x DV fp32) is rows 0-15 in sK0 and
   // rows 16-31 in sV0, its row max / sum in sK1 (sKq0 for Q8).
-  static_assert(!Q8 || (DQK == 128 && DV == 128), "int8 K/V: head dim 128");
+  static_assert(!Q8 || (DQK == 128 && DV == 128), "quantized K/V: head dim 128");
   static_assert(16 * DV * 4 <= BC * DV * 2, "half an O partial fits a V tile");
   __shared__ __attribute__((aligned(1024))) T sK0[4][BC * DQK];
   __shared__ __attribute__((aligned(1024))) T sK1[4][Q8 ? 1 : BC * DQK];
@@ -149,6 +227,8 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   // moved as rows of D/2 16-bit elements)
   using LT = std::conditional_t<Q8, uint16_t, T>;
   constexpr int LDQK = Q8 ? DQK / 2 : DQK, LDV = Q8 ? DV / 2 : DV;
+  using KLoader = std::conditional_t<Q4, Int4TileLoader<DQK>, TileLoader<LDQK, BC, LT, 1>>;
+  using VLoader = std::conditional_t<Q4, Int4TileLoader<DV>, TileLoader<LDV, BC, LT, 1>>;
   T* const kd = sK0[w];  // Q8: dequantized K tile
   T* const vd = sV0[w];  // Q8: dequantized V tile
   // the tiles the loads fill (buf a compile-time constant)
@@ -162,9 +242,15 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
     if constexpr (Q8) return buf ? sVq1[w] : sVq0[w];
     else return buf ? sV1[w] : sV0[w];
   };
-  TileLoader<LDQK, BC, LT, 1> ldK;
-  TileLoader<LDV, BC, LT, 1> ldV;
-  if constexpr (Q8) {
+  KLoader ldK;
+  VLoader ldV;
+  if constexpr (Q4) {
+    // strides count bytes
+    const int8_t* kq = (const int8_t*)a.k + sp.bsel * a.sk_.b + (int64_t)hk * a.sk_.h + sp.ktok * a.sk_.s;
+    const int8_t* vq = (const int8_t*)a.v + sp.bsel * a.sv_.b + (int64_t)hk * a.sv_.h + sp.ktok * a.sv_.s;
+    ldK.init(kq, a.sk_.s, 0, lane);
+    ldV.init(vq, a.sv_.s, 0, lane);
+  } else if constexpr (Q8) {
     const int8_t* kq = (const int8_t*)a.k + sp.bsel * a.sk_.b + (int64_t)hk * a.sk_.h + sp.ktok * a.sk_.s;
     const int8_t* vq = (const int8_t*)a.v + sp.bsel * a.sv_.b + (int64_t)hk * a.sv_.h + sp.ktok * a.sv_.s;
     ldK.init((const LT*)kq, a.sk_.s / 2, 0, lane);
@@ -173,13 +259,16 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
     ldK.init(base_ptr<LT>(a.k, a.sk_, sp, hk, false), a.sk_.s, 0, lane);
     ldV.init(base_ptr<LT>(a.v, a.sv_, sp, hk, false), a.sv_.s, 0, lane);
   }
-  // Q8: this lane's scale / zero point column (its chunk's group) and the
-  // per-token scale rows of this sequence and key/value head
-  const int qcol = Q8 ? (16 * (lane & 7)) / d.qgs : 0;
+  // Quantized K/V: a lane dequantizes chunks of CPC codes, LPR lanes per
+  // row, at rows lane / LPR + RSTEP u (u < NSC).  This lane's scale / zero
+  // point column (its chunk's group) and the per-token scale rows of this
+  // sequence and key/value head:
+  constexpr int CPC = Q4 ? 32 : 16, LPR = DQK / CPC, RSTEP = 64 / LPR, NSC = Q4 ? 2 : 4;
+  const int qcol = Q8 ? (CPC * (lane % LPR)) / d.qgs : 0;
   const int64_t sc_base = sp.bsel * d.ss.b + (int64_t)hk * d.ss.h + sp.ktok * d.ss.s + qcol;
-  // this lane's scale (zero point) entries for tile row lane / 8; a tile's
-  // row u-th group then only adds the uniform (n0 + 8u) rows
-  const int64_t sc_lane = sc_base + (int64_t)(lane >> 3) * d.ss.s;
+  // this lane's scale (zero point) entries for tile row lane / LPR; the
+  // lane's u-th row then only adds the uniform (n0 + RSTEP u) rows
+  const int64_t sc_lane = sc_base + (int64_t)(lane / LPR) * d.ss.s;
   float ksc[2][4], vsc[2][4];
   int kzp[2][4], vzp[2][4];
   // (buf is a compile-time constant: the scale registers are indexed by it)
@@ -191,30 +280,30 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
       if (n0 + BC <= skv) {
         // whole tile in range: per-lane offset plus a uniform row offset
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t o = sc_lane + (int64_t)(n0 + 8 * u) * d.ss.s;
+        for (int u = 0; u < NSC; ++u) {
+          const int64_t o = sc_lane + (int64_t)(n0 + RSTEP * u) * d.ss.s;
           ksc[buf][u] = d.k_sc[o];
           vsc[buf][u] = d.v_sc[o];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t o = sc_lane + (int64_t)(n0 + 8 * u) * d.ss.s;
-          kzp[buf][u] = QM == 2 ? d.k_zp[o] : 0;
-          vzp[buf][u] = QM == 2 ? d.v_zp[o] : 0;
+        for (int u = 0; u < NSC; ++u) {
+          const int64_t o = sc_lane + (int64_t)(n0 + RSTEP * u) * d.ss.s;
+          kzp[buf][u] = QZP ? d.k_zp[o] : 0;
+          vzp[buf][u] = QZP ? d.v_zp[o] : 0;
         }
       } else {
         // the last tile: rows clamped to the sequence (those keys are masked)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
+        for (int u = 0; u < NSC; ++u) {
+          const int row = min(n0 + lane / LPR + RSTEP * u, skv - 1);
           ksc[buf][u] = d.k_sc[sc_base + (int64_t)row * d.ss.s];
           vsc[buf][u] = d.v_sc[sc_base + (int64_t)row * d.ss.s];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int row = min(n0 + (lane >> 3) + 8 * u, skv - 1);
-          kzp[buf][u] = QM == 2 ? d.k_zp[sc_base + (int64_t)row * d.ss.s] : 0;
-          vzp[buf][u] = QM == 2 ? d.v_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+        for (int u = 0; u < NSC; ++u) {
+          const int row = min(n0 + lane / LPR + RSTEP * u, skv - 1);
+          kzp[buf][u] = QZP ? d.k_zp[sc_base + (int64_t)row * d.ss.s] : 0;
+          vzp[buf][u] = QZP ? d.v_zp[sc_base + (int64_t)row * d.ss.s] : 0;
         }
       }
     }
@@ -222,9 +311,9 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
   if (ntw > 0) load_tile(std::integral_constant<int, 0>{}, (tb + w) * BC);
   if (ntw > 1) load_tile(std::integral_constant<int, 1>{}, (tb + w + 4) * BC);
   // vector memory operations of one tile (K and V direct-to-LDS loads, and
-  // the scales and zero points of int8 K/V)
-  constexpr int TILE_LOADS = TileLoader<LDQK, BC, LT, 1>::PER_WAVE +
-                             TileLoader<LDV, BC, LT, 1>::PER_WAVE + 8 * QM;
+  // the scales and zero points of quantized K/V)
+  constexpr int TILE_LOADS =
+      KLoader::PER_WAVE + VLoader::PER_WAVE + (Q8 ? 2 * NSC * (QZP ? 2 : 1) : 0);
 
   const float c = a.scale_log2;
   // a zero scale cannot hide a score with an infinity through the FMA: such
@@ -253,9 +342,15 @@ __global__ void __launch_bounds__(256, 1) fwd_decode(const FwdArgs a, const Deco
     else wait_vm<0>();
     const T* cK;
     const T* cV;
-    if constexpr (Q8) {
+    if constexpr (Q4) {
+      constexpr bool SG = QM <= 4;  // signed codes
+      dequant_tile4<T, DQK, SG>((const uint8_t*)ktile(bufc), kd, ksc[buf], kzp[buf], lane);
+      dequant_tile4<T, DV, SG>((const uint8_t*)vtile(bufc), vd, vsc[buf], vzp[buf], lane);
+    } else if constexpr (Q8) {
       dequant_tile<T, DQK>(ktile(bufc), kd, ksc[buf], kzp[buf], lane);
       dequant_tile<T, DV>(vtile(bufc), vd, vsc[buf], vzp[buf], lane);
+    }
+    if constexpr (Q8) {
       wait_lds();  // the 16-bit tiles are written, the staging tiles read
       if (j + 2 < ntw) load_tile(bufc, n0 + 8 * BC);
       cK = kd;
@@ -461,12 +556,15 @@ template <typename T, int DQK, int DV>
 static hipError_t decode_dims(bool band, const FwdArgs& a, const DecodeArgs& d, hipStream_t st) {
   const int64_t units = (int64_t)a.B * (a.H / a.G) * d.ns * d.rg;
   dim3 grid((unsigned)(8 * ((units + 7) / 8))), block(256);
-  const int qm = d.k_sc == nullptr ? 0 : (d.k_zp == nullptr ? 1 : 2);
+  // kernel code format: 0 16-bit; 1 int8, 3 signed 4-bit, 5 unsigned 4-bit;
+  // one more with zero points
+  const int qm = d.k_sc == nullptr ? 0 : (2 * d.qfmt - 1 + (d.k_zp != nullptr ? 1 : 0));
   if constexpr (DQK == 128 && DV == 128) {
-    if (qm == 1 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 1>), grid, block, 0, st, a, d);
-    if (qm == 1 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 1>), grid, block, 0, st, a, d);
-    if (qm == 2 && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, 2>), grid, block, 0, st, a, d);
-    if (qm == 2 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 2>), grid, block, 0, st, a, d);
+#define SDPA_DEC_Q(QMV)                                                                            \
+    if (qm == QMV && band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, true, QMV>), grid, block, 0, st, a, d); \
+    if (qm == QMV && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, QMV>), grid, block, 0, st, a, d);
+    SDPA_DEC_Q(1) SDPA_DEC_Q(2) SDPA_DEC_Q(3) SDPA_DEC_Q(4) SDPA_DEC_Q(5) SDPA_DEC_Q(6)
+#undef SDPA_DEC_Q
   } else if (qm != 0) {
     return hipErrorInvalidValue;
   }
@@ -474,8 +572,8 @@ static hipError_t decode_dims(bool band, const FwdArgs& a, const DecodeArgs& d, 
   if (qm == 0 && !band) hipLaunchKernelGGL((fwd_decode<T, DQK, DV, false, 0>), grid, block, 0, st, a, d);
   if (log_enabled()) {
     char tile[128];
-    std::snprintf(tile, sizeof(tile), "%d row groups of 32 x %d splits of %d keys, int8 K/V %d", d.rg,
-                  d.ns, d.chunk, qm);
+    std::snprintf(tile, sizeof(tile), "%d row groups of 32 x %d splits of %d keys, K/V codes %d",
+                  d.rg, d.ns, d.chunk, qm);
     log_launch("fwd_decode", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV,
                band, false, false, tile, grid, block);
   }

@@ -94,13 +94,15 @@ struct DecodeArgs {
   int32_t ns;       // splits
   int32_t chunk;    // keys per split, a multiple of 128
   int32_t rg;       // 32-row groups of (query head of the group, position) pairs
-  // int8 K/V (k_sc non-null; a.k, a.v then hold int8 codes with byte
-  // strides): per (token, group of qgs head-dim elements) fp32 scales and
-  // nullable int8 zero points, at element strides ss (group index unit)
+  // quantized K/V (k_sc non-null; a.k, a.v then hold int8 codes, or 4-bit
+  // codes two per byte, with byte strides): per (token, group of qgs
+  // head-dim elements) fp32 scales and nullable int8 zero points, at element
+  // strides ss (group index unit)
   const float *k_sc, *v_sc;
   const int8_t *k_zp, *v_zp;
   Str ss;
   int32_t qgs;
+  int32_t qfmt;  // codes: 1 int8, 2 signed 4-bit, 3 unsigned 4-bit (0: 16-bit K/V)
 };
 struct DecodePlan {
   int32_t ns, chunk, rg;

@@ -11,13 +11,16 @@ dtype (round to nearest even).  Tensors are dense BHSD (batch mode) or packed
 THD with cu_seqlens = [0, cumsum(lengths)] (group mode); K and V use the
 same lengths unless explicit key/value lengths are given.
 
-Quantized K/V (kv_quant = (group_size, with_zero_points)): K and V are int8
-codes clip(round(40 z), -127, 127), z standard normal, with fp32 scales
-U(0.02, 0.03) per token and group of head-dim elements (about what a
-per-group max-abs quantizer gives for N(0, 1) data) and, optionally, int8
-zero points randint(-8, 9); drawn in the order codes K, scales K, [zero
-points K], codes V, scales V, [zero points V], in place of the K and V
-normals.
+Quantized K/V (kv_quant = (group_size, with_zero_points[, format])): with
+format "s8" (the default) K and V are int8 codes clip(round(40 z), -127,
+127), z standard normal, with fp32 scales U(0.02, 0.03) per token and group
+of head-dim elements (about what a per-group max-abs quantizer gives for
+N(0, 1) data) and, optionally, int8 zero points randint(-8, 9); drawn in the
+order codes K, scales K, [zero points K], codes V, scales V, [zero points V],
+in place of the K and V normals.  With format "s4" the codes are
+clip(round(3.5 z), -8, 7), with "u4" that plus 8, clipped to 0 .. 15, the
+scales U(0.25, 0.32), and the codes are stored two per byte, code 2i in the
+low nibble of byte i (uint8 tensors with a last dimension of d / 2).
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -53,7 +56,7 @@ class Workload:
     bottom_right: bool = False
     window_left: Optional[int] = None
     window_right: Optional[int] = None
-    kv_quant: Optional[tuple] = None  # (group_size, with_zero_points): int8 K/V codes
+    kv_quant: Optional[tuple] = None  # (group_size, with_zero_points[, "s8" | "s4" | "u4"])
     extra: dict = field(default_factory=dict)
 
     @property
@@ -85,6 +88,11 @@ DECODE = Workload("bf16 decode B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1
 DECODE_Q8 = Workload("bf16 decode int8-KV g32 B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1,
                      8192, 128, 128, causal=True, bottom_right=True, h_kv=8, seed=1007,
                      kv_quant=(32, False))
+# And over a signed 4-bit K/V cache (two codes per byte), scales per token
+# and group of 32 head-dim elements, no zero points.
+DECODE_Q4 = Workload("bf16 decode int4-KV g32 B16 H32 Hkv8 Sq1 Skv8192 d128", "bf16", 16, 32, 1,
+                     8192, 128, 128, causal=True, bottom_right=True, h_kv=8, seed=1008,
+                     kv_quant=(32, False, "s4"))
 
 
 def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
@@ -128,12 +136,20 @@ def make_inputs(wl: Workload, lengths=None, kv_lengths=None):
         out["k"] = torch.randn(shp_k, generator=g, dtype=torch.float32).to(io)
         out["v"] = torch.randn(shp_v, generator=g, dtype=torch.float32).to(io)
     else:
-        gs, with_zp = wl.kv_quant
+        gs, with_zp = wl.kv_quant[:2]
+        fmt = wl.kv_quant[2] if len(wl.kv_quant) > 2 else "s8"
         for name, shp in (("k", shp_k), ("v", shp_v)):
             z = torch.randn(shp, generator=g, dtype=torch.float32)
-            out[name] = torch.clamp(torch.round(40.0 * z), -127, 127).to(torch.int8)
             sshp = shp[:-1] + (shp[-1] // gs,)
-            out[name + "_scales"] = 0.02 + 0.01 * torch.rand(sshp, generator=g, dtype=torch.float32)
+            if fmt == "s8":
+                out[name] = torch.clamp(torch.round(40.0 * z), -127, 127).to(torch.int8)
+                out[name + "_scales"] = 0.02 + 0.01 * torch.rand(sshp, generator=g, dtype=torch.float32)
+            else:
+                c = torch.round(3.5 * z)
+                c = torch.clamp(c, -8, 7) if fmt == "s4" else torch.clamp(c + 8, 0, 15)
+                nib = (c.to(torch.int64) & 15).to(torch.uint8)  # storage: low nibble first
+                out[name] = nib[..., 0::2] | (nib[..., 1::2] << 4)
+                out[name + "_scales"] = 0.25 + 0.07 * torch.rand(sshp, generator=g, dtype=torch.float32)
             out[name + "_zp"] = (torch.randint(-8, 9, sshp, generator=g).to(torch.int8)
                                  if with_zp else None)
     if wl.bias:

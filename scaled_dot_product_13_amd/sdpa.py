@@ -142,17 +142,21 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _check_operands(q, k=None, v=None, *, quant_kv=False, cu=(), same=()):
+KV_QUANT = {"s8": 1, "s4": 2, "u4": 3}  # SDPA_KV_QUANT_S8 / _S4 / _U4
+
+
+def _check_operands(q, k=None, v=None, *, quant_kv=None, cu=(), same=()):
     """Raise TypeError unless every operand is on q's device with q's dtype
-    (k, v: int8 codes when quant_kv) and every cu_seqlens array is a
-    contiguous int32 tensor there: the library reads raw bytes, so a wrong
-    dtype would otherwise give wrong results with no error."""
+    (k, v: int8 codes for quant_kv "s8", uint8 bytes of two 4-bit codes for
+    "s4" / "u4") and every cu_seqlens array is a contiguous int32 tensor
+    there: the library reads raw bytes, so a wrong dtype would otherwise give
+    wrong results with no error."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("k", k), ("v", v)):
         if t is None:
             continue
-        want = torch.int8 if quant_kv else q.dtype
+        want = (q.dtype if quant_kv is None else torch.int8 if quant_kv == "s8" else torch.uint8)
         if t.dtype != want or t.device != q.device:
             raise TypeError(f"{name} must be {want} on {q.device}, got {t.dtype} on {t.device}")
     for name, t in same:
@@ -166,7 +170,8 @@ def _check_operands(q, k=None, v=None, *, quant_kv=False, cu=(), same=()):
 def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, offset=0,
                  seed_offset=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
                  max_seqlen_kv=None, bottom_right=False, window_left=None, window_right=None,
-                 alibi_slopes=None, kv_scales=None, kv_zero_points=None, kv_group_size=None):
+                 alibi_slopes=None, kv_scales=None, kv_zero_points=None, kv_group_size=None,
+                 kv_format=None):
     """Fill the C problem struct from tensor shapes (batch [B,H,S,D] or group
     [T,H,D]); k and v may have fewer heads than q (grouped-query attention).
 
@@ -178,11 +183,19 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
     adds -slope |j - i - off'| to the scores, off' the mask's alignment
     (bottom-right without a mask).  The tensor must outlive the call.
 
-    int8 K/V: k and v are int8 codes; kv_scales = (k_scales, v_scales),
-    fp32 [.., tokens, d / kv_group_size] laid out like k without its last
-    dimension (batch [B, Hkv, S, G] or group [T, Hkv, G]); kv_zero_points
-    likewise int8, or None."""
-    _check_operands(q, k, v, quant_kv=kv_scales is not None,
+    Quantized K/V: kv_scales = (k_scales, v_scales), fp32 [.., tokens,
+    d / kv_group_size] laid out like k without its last dimension (batch
+    [B, Hkv, S, G] or group [T, Hkv, G]); kv_zero_points likewise int8, or
+    None.  k and v are int8 codes (kv_format "s8", the default for int8
+    tensors) or uint8 tensors of packed 4-bit codes, two per byte with the
+    low nibble first (kv_format "s4" signed or "u4" unsigned; the last
+    dimension is then d / 2)."""
+    fmt = None
+    if kv_scales is not None:
+        fmt = kv_format or ("s8" if k.dtype == torch.int8 else None)
+        if fmt not in KV_QUANT:
+            raise TypeError("kv_format must be 's8', 's4' or 'u4' (uint8 K/V need 's4' or 'u4')")
+    _check_operands(q, k, v, quant_kv=fmt,
                     cu=(("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)))
     if seed_offset is not None and (seed_offset.dtype not in (torch.int64, torch.uint64)
                                     or seed_offset.numel() < 2 or seed_offset.device != q.device):
@@ -222,7 +235,9 @@ def make_problem(q, k, v, *, scale=None, causal=False, dropout_p=0.0, seed=0, of
         if (ks.dtype != torch.float32 or vs.dtype != torch.float32 or ks.stride() != vs.stride()
                 or ks.device != q.device or vs.device != q.device):
             raise TypeError("kv_scales: two float32 tensors on q's device with equal strides")
-        p.kv_quant = 1
+        p.kv_quant = KV_QUANT[fmt]
+        if fmt != "s8":
+            p.d_v = 2 * v.shape[-1]  # two codes per byte
         p.kv_group_size = int(kv_group_size)
         p.k_scales, p.v_scales = ks.data_ptr(), vs.data_ptr()
         p.kv_scale_strides = _strides(ks, group)
@@ -246,7 +261,7 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
              max_seqlen_kv=None, return_lse=True, return_keep=False, out=None, lse=None,
              bottom_right=False, window_left=None, window_right=None, split_kv=True,
              workspace=None, alibi_slopes=None, kv_scales=None, kv_zero_points=None,
-             kv_group_size=None):
+             kv_group_size=None, kv_format=None):
     """Forward.  Returns (o, lse or None, keep or None).  split_kv=False
     passes no workspace, so a thin-query problem runs unsplit; `workspace`
     (uint8, at least fwd_workspace_size bytes) avoids an allocation."""
@@ -257,13 +272,14 @@ def sdpa_fwd(q, k, v, *, bias=None, scale=None, causal=False, dropout_p=0.0, see
                      max_seqlen_kv=max_seqlen_kv, bottom_right=bottom_right,
                      window_left=window_left, window_right=window_right,
                      alibi_slopes=alibi_slopes, kv_scales=kv_scales,
-                     kv_zero_points=kv_zero_points, kv_group_size=kv_group_size)
+                     kv_zero_points=kv_zero_points, kv_group_size=kv_group_size,
+                     kv_format=kv_format)
     _check_operands(q, same=(("bias", bias), ("out", out)))
     if lse is not None and (lse.dtype != torch.float32 or lse.device != q.device):
         raise TypeError("lse must be float32 on q's device")
     if out is None:
         oshape = list(q.shape)
-        oshape[-1] = v.shape[-1]
+        oshape[-1] = p.d_v
         out = _alloc_like(q, oshape)
     if return_lse and lse is None:
         lse = (torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device) if group

@@ -131,6 +131,13 @@ def test_invalid_arguments(S):
     assert _fwd(S, _problem(S, q8=32, s_q=1, d_qk=64, d_v=64)) == S.SDPA_ERR_UNSUPPORTED
     assert _bwd(S, _problem(S, q8=32, s_q=1)) == S.SDPA_ERR_UNSUPPORTED
     assert b"forward" in L.sdpa_last_error_message()
+    # 4-bit codes: one scale group per 32-code chunk, so g >= 32
+    q4 = _problem(S, q8=16, s_q=1)
+    q4.kv_quant = 2
+    assert _fwd(S, q4) == S.SDPA_ERR_UNSUPPORTED
+    assert b"kv_group_size" in L.sdpa_last_error_message()
+    q4.kv_quant = 4
+    assert _fwd(S, q4) == S.SDPA_ERR_INVALID_ARG
 
 
 def test_problem_struct_matches_the_header(S):

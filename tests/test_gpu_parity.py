@@ -389,10 +389,12 @@ def test_alibi_varlen(S):
 
 
 def run_q8(S, wl, lengths=None, kv_lengths=None, split=True):
-    """Thin-query forward over int8 K/V codes against the oracle's forward on
-    the dequantized K and V (fp64)."""
+    """Thin-query forward over quantized K/V codes (int8, or 4-bit two per
+    byte) against the oracle's forward on the dequantized K and V (fp64;
+    4-bit codes unpacked by the oracle)."""
     x = inputs.make_inputs(wl, lengths, kv_lengths)
-    gs, with_zp = wl.kv_quant
+    gs, with_zp = wl.kv_quant[:2]
+    fmt = wl.kv_quant[2] if len(wl.kv_quant) > 2 else "s8"
     group = wl.varlen is not None
     dev = "cuda"
     g = {n: x[n].to(dev) for n in ("q", "k", "v", "k_scales", "v_scales")}
@@ -405,12 +407,15 @@ def run_q8(S, wl, lengths=None, kv_lengths=None, split=True):
                   max_seqlen_q=x["max_seqlen"], max_seqlen_kv=x["max_seqlen_kv"])
         okw.update(cu_seqlens_q=x["cu_seqlens"].numpy().astype(np.int64),
                    cu_seqlens_kv=x["cu_seqlens_kv"].numpy().astype(np.int64))
-    _say("int8 K/V", wl.dtype, "B", wl.b, "H", wl.h, "Hkv", wl.h_kv, "Sq", wl.s_q, "Skv", wl.s_kv,
-         "group size", gs, "zero points", with_zp, "varlen", group, "split", split, kw.get("causal"))
+    _say("quantized K/V", fmt, wl.dtype, "B", wl.b, "H", wl.h, "Hkv", wl.h_kv, "Sq", wl.s_q,
+         "Skv", wl.s_kv, "group size", gs, "zero points", with_zp, "varlen", group, "split", split,
+         kw.get("causal"))
     o, lse, _ = S.sdpa_fwd(g["q"], g["k"], g["v"], kv_scales=(g["k_scales"], g["v_scales"]),
-                           kv_zero_points=zp, kv_group_size=gs, split_kv=split, **kw)
+                           kv_zero_points=zp, kv_group_size=gs, split_kv=split, kv_format=fmt, **kw)
     torch.cuda.synchronize()
-    deq = {n: O.dequantize_kv(x[n].numpy(), x[n + "_scales"].numpy(), gs,
+    codes = {n: (x[n].numpy() if fmt == "s8" else O.unpack_int4(x[n].numpy(), fmt == "s4"))
+             for n in ("k", "v")}
+    deq = {n: O.dequantize_kv(codes[n], x[n + "_scales"].numpy(), gs,
                               x[n + "_zp"].numpy() if with_zp else None) for n in ("k", "v")}
     ref = O.fwd(x["q"].double().numpy(), deq["k"], deq["v"], **okw)
     errs = {"o": _cmp("o", _np(o), ref["o"], x["dtype"])}
@@ -465,6 +470,35 @@ def test_int8_kv_varlen(S):
 
 def test_int8_kv_decode_workload_full(S):
     run_q8(S, inputs.DECODE_Q8)
+
+
+Q4 = [
+    # dtype, s_q, s_kv, h, h_kv, group size, zero points, format, causal, window_left, split
+    ("bf16", 1, 1000, 8, 2, 32, False, "s4", True, None, True),
+    ("f16", 4, 777, 8, 2, 64, True, "s4", True, 100, True),
+    ("bf16", 16, 2081, 16, 2, 128, True, "u4", True, None, False),  # 4 row groups, unsplit
+    ("bf16", 1, 17, 4, 1, 32, True, "u4", False, None, True),
+    ("f16", 3, 600, 6, 3, 32, False, "u4", False, None, True),
+]
+
+
+@pytest.mark.parametrize("case", Q4, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-h{c[3]}kv{c[4]}-g{c[5]}"
+                         f"-zp{int(c[6])}-{c[7]}-c{int(c[8])}-w{c[9]}-split{int(c[10])}")
+def test_int4_kv_thin_query_parity(S, case):
+    dt, sq, skv, h, hkv, gs, zp, fmt, causal, wl_, split = case
+    wl = inputs.small(dt, b=2, h=h, h_kv=hkv, s_q=sq, s_kv=skv, causal=causal, bottom_right=True,
+                      window_left=wl_, seed=sq * 17 + skv, kv_quant=(gs, zp, fmt))
+    run_q8(S, wl, split=split)
+
+
+def test_int4_kv_varlen(S):
+    wl = inputs.small("bf16", b=3, h=8, h_kv=2, causal=True, bottom_right=True, seed=43,
+                      varlen=(3, 1, 1), kv_quant=(64, True, "s4"))
+    run_q8(S, wl, lengths=[1, 1, 2], kv_lengths=[1, 700, 3000])
+
+
+def test_int4_kv_decode_workload_full(S):
+    run_q8(S, inputs.DECODE_Q4)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-d{c[1][0]}x{c[1][1]}-{c[2]}x{c[3]}"
