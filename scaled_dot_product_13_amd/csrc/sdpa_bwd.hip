@@ -109,8 +109,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T sO[NSET][BQ * DV];
   __shared__ __attribute__((aligned(1024))) T sB[BIAS_LDS ? NSET : 1][BIAS_LDS ? BQ * BC : 64];
   __shared__ __attribute__((aligned(256))) float sL[NSET][BQ], sD[NSET][BQ];
-  // P from role A to role B: [slot][key block][4 groups of 4 elements][lane]
-  __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];
+  // P from role A to role B in the io type: [slot][key block][2 groups of 8
+  // elements][lane]
+  __shared__ __attribute__((aligned(1024))) u32x4 sP[2][4][2][64];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
@@ -240,9 +241,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   rdOt.init(lane);
   rdO.init(lane);
   rdQt.init(lane);
-  // this lane's P slot: 4 x 16 bytes at stride 1 KiB
+  // this lane's P slot: 2 x 16 bytes at stride 1 KiB
   const uint32_t p_lane = lds_addr(&sP[0][kb][0][0]) + 16 * lane;
-  constexpr uint32_t P_SLOT = 4 * 4 * 64 * 16;
+  constexpr uint32_t P_SLOT = 4 * 2 * 64 * 16;
 
   // ---- role A: S, P, dV for tile i -----------------------------------------
   auto stepA = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
@@ -320,33 +321,34 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         pv[r] = vis ? pv[r] : 0.f;
       }
     }
-    // hand P to role B: dropped elements carry the sign bit
+    // hand P to role B in the io type (P >= 0, so under dropout the sign bit
+    // of each element marks it dropped); pb is P o Z for the dV product
     u32x4 pb[2];
     {
-      uint32_t bits[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bits[r] = __float_as_uint(pv[r]);
-        if (DROP) {
-          const int k = 2 * (r >> 3) + ((r & 7) >> 2);
-          const bool keep = ((kw[k] >> (8 * (r & 3))) & 0xffu) >= dk.thr;
-          bits[r] |= keep ? 0u : 0x80000000u;
-        }
-      }
-      const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(pa + 1024 * j) =
-            u32x4{bits[4 * j], bits[4 * j + 1], bits[4 * j + 2], bits[4 * j + 3]};
+      u32x4 ph[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * tt + 2 * e;
-          const float p0 = DROP ? ((bits[r] >> 31) ? 0.f : pv[r]) : pv[r];
-          const float p1 = DROP ? ((bits[r + 1] >> 31) ? 0.f : pv[r + 1]) : pv[r + 1];
-          pb[tt][e] = pack2<T>(p0, p1);
+          const uint32_t wd = pack2<T>(pv[r], pv[r + 1]);
+          if (DROP) {
+            uint32_t keep[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int k = 2 * ((r + u) >> 3) + (((r + u) & 7) >> 2);
+              keep[u] = ((kw[k] >> (8 * ((r + u) & 3))) & 0xffu) >= dk.thr;
+            }
+            ph[tt][e] = wd | (keep[0] ? 0u : 0x8000u) | (keep[1] ? 0u : 0x80000000u);
+            pb[tt][e] = wd & ((keep[0] ? 0xffffu : 0u) | (keep[1] ? 0xffff0000u : 0u));
+          } else {
+            ph[tt][e] = wd;
+            pb[tt][e] = wd;
+          }
         }
+      const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(pa + 1024 * j) = ph[j];
     }
     // dV^T += dO^T (P o Z)
     if constexpr (!EARLY_O) read_oop();
@@ -382,9 +384,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + qb] = vQt.template read<32 * qb>(16 * tt);
     });
     const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
-    u32x4 pw[4];
+    u32x4 pw[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pw[j] = lds_load16(pa + 1024 * j);
+    for (int j = 0; j < 2; ++j) pw[j] = lds_load16(pa + 1024 * j);
     const float* cD = sD[set];
     u32x4 dsb[2];
 #pragma unroll
@@ -395,14 +397,15 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * hh + e;
-        const uint32_t bits = pw[r >> 2][r & 3];
+        const uint32_t wd = pw[hh][e >> 1];
+        const uint32_t bits = (e & 1) ? wd >> 16 : wd & 0xffffu;
         const float Dq = e < 4 ? D0[e] : D1[e - 4];
         float p, dpz;
         if (DROP) {
-          p = __uint_as_float(bits & 0x7fffffffu);
-          dpz = (bits >> 31) ? 0.f : dp[r] * rescale;
+          p = to_f32<T>((uint16_t)(bits & 0x7fffu));
+          dpz = (bits >> 15) ? 0.f : dp[r] * rescale;
         } else {
-          p = __uint_as_float(bits);
+          p = to_f32<T>((uint16_t)bits);
           dpz = dp[r];
         }
         ds[e] = p * (dpz - Dq);
@@ -607,8 +610,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
 #pragma unroll
   for (int i = 0; i < QB; ++i) dqacc[i] = f32x16{};
 
-  TileLoader<DQK, BC, T> ldK;
-  TileLoader<DV, BC, T> ldV;
+  TileLoader<DQK, BC, T, 4, true> ldK;
+  TileLoader<DV, BC, T, 4, true> ldV;
   ldK.init(kg, a.sk_.s, w, lane);
   ldV.init(vg, a.sv_.s, w, lane);
   if (nt > 0) {

@@ -127,14 +127,24 @@ typedef __attribute__((address_space(3))) void lds_void;
 // to row_limit - 1 (callers mask those rows), so every address is valid;
 // row_limit must be >= 1.  NW waves (w = 0 .. NW-1) share the loads; `w`
 // must be wave-uniform.
-template <int D, int ROWS, typename T, int NW = 4> struct TileLoader {
+// PIN: add each lane's 32-bit offset to the uniform tile base at the load
+// (scalar-base addressing) rather than letting the compiler keep one 64-bit
+// address per load live across the key loop; for kernels whose register
+// budget is tight.
+template <int D, int ROWS, typename T, int NW = 4, bool PIN = false> struct TileLoader {
   static constexpr int CPR = Lds<D>::CPR;
   static constexpr int PER_WAVE = ROWS * CPR / (64 * NW);
   static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
   static constexpr int LOWMASK = (D % 128 == 0) ? 15 : 7;
+  // When one load's 64 NW chunks are whole rows and a multiple of the
+  // swizzle period (16 rows), load j covers load 0's pattern RSTEP j rows
+  // further down: one per-lane offset serves all loads and the row step goes
+  // into the uniform base.
+  static constexpr bool AFFINE = (64 * NW) % CPR == 0 && (64 * NW / CPR) % 16 == 0;
+  static constexpr int RSTEP = AFFINE ? 64 * NW / CPR : 0;
   const char* g;
   int64_t stride_b;  // row stride in bytes
-  uint32_t voff[PER_WAVE];
+  uint32_t voff[AFFINE ? 1 : PER_WAVE];
 
   __device__ __forceinline__ static void coords(int j, int w, int lane, int& row, int& c) {
     const int L = 64 * (NW * j + w) + lane;
@@ -146,7 +156,7 @@ template <int D, int ROWS, typename T, int NW = 4> struct TileLoader {
     g = (const char*)g_;
     stride_b = row_stride * (int64_t)sizeof(T);
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
+    for (int j = 0; j < (AFFINE ? 1 : PER_WAVE); ++j) {
       int row, c;
       coords(j, w, lane, row, c);
       voff[j] = (uint32_t)(row * stride_b + 16 * c);
@@ -156,9 +166,13 @@ template <int D, int ROWS, typename T, int NW = 4> struct TileLoader {
     if (row0 + ROWS <= row_limit) {
       const char* base = g + row0 * stride_b;
 #pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j)
-        __builtin_amdgcn_global_load_lds((const void*)(base + voff[j]),
+      for (int j = 0; j < PER_WAVE; ++j) {
+        uint32_t o = voff[AFFINE ? 0 : j];
+        if (PIN) __asm__ volatile("" : "+v"(o));  // opaque: the add cannot be hoisted
+        const char* bj = AFFINE ? base + (int64_t)(RSTEP * j) * stride_b : base;
+        __builtin_amdgcn_global_load_lds((const void*)(bj + o),
                                          (lds_void*)(tile + 512 * (NW * j + w)), 16, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
@@ -387,7 +401,14 @@ __device__ __forceinline__ void quad_keep_words(const uint32_t var4[8], uint32_t
   uint32_t w[2][4];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    uint32_t v4 = var4[2 * c + s];
+    // var4[2c + s] by selects on register copies (the compiler turns a
+    // lane-dependent index, or selects of array elements, into a load from
+    // scratch memory)
+    uint32_t a0 = var4[s], a1 = var4[2 + s], a2 = var4[4 + s], a3 = var4[6 + s];
+    __asm__ volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    uint32_t v4 = (c == 1) ? a1 : a0;
+    v4 = (c == 2) ? a2 : v4;
+    v4 = (c == 3) ? a3 : v4;
     if (ROW_FIXED)
       Philox::block(v4, fix4, bh, off, k0, k1, w[s]);
     else

@@ -31,13 +31,25 @@
 
 namespace sdpa {
 
+// Wide head dims (d_qk + d_v > 256) without dropout read their K and V
+// operands as they use them (LEAN) instead of a whole tile's ahead: the
+// prefetched operands alone (d 192/128: 96 + 64 registers) would hold the
+// kernel at one wave per SIMD, where nothing hides the latency of its
+// loads.  With LEAN the second wave on the SIMD hides it.
+template <int DQK, int DV, bool DROP> struct FwdLean {
+  static constexpr bool value = (DQK + DV > 256) && !DROP;
+};
 // workgroups per CU the register budget is sized for
-// Two waves per SIMD (256 registers) unless the head dims are wide.  With
-// dropout the d 128 instances spill at that budget; the causal ones without
-// bias still run faster at two waves (measured), the others keep one wave.
+// Two waves per SIMD (256 registers) unless the head dims are wide (and not
+// LEAN).  With dropout the d 128 instances spill at that budget; the causal
+// ones without bias still run faster at two waves (measured), the others
+// keep one wave.
 template <int DQK, int DV, bool DROP, bool BAND = false, bool BIAS = false> struct FwdOcc {
   static constexpr int value =
-      (DQK + DV > 256) || (DROP && DQK + DV > 128 && !(BAND && !BIAS)) ? 1 : 2;
+      ((DQK + DV > 256) && !FwdLean<DQK, DV, DROP>::value) ||
+              (DROP && DQK + DV > 128 && !(BAND && !BIAS))
+          ? 1
+          : 2;
 };
 
 template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
@@ -163,9 +175,11 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     const bool active = !BAND || (n0 <= wq0 + 31 + bd.hi && n0 + BC - 1 >= wq0 + bd.lo);
 
     // All K operands of this tile are requested first, so their LDS latency
-    // overlaps the prefetch issue and the rest of the requests.
-    u32x4 kop[NBLK * KT];
-    if (active) {
+    // overlaps the prefetch issue and the rest of the requests (LEAN: each
+    // is read at its product).
+    constexpr bool LEAN = FwdLean<DQK, DV, DROP>::value;
+    u32x4 kop[LEAN ? 1 : NBLK * KT];
+    if (!LEAN && active) {
       static_for<KT>([&](auto t) __attribute__((always_inline)) {
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = rdK.template read<t>(cK, 32 * blk);
@@ -193,10 +207,18 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     f32x16 s[NBLK];
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) s[blk] = f32x16{};
+    if constexpr (LEAN) {
+      static_for<KT>([&](auto t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+        for (int blk = 0; blk < NBLK; ++blk)
+          s[blk] = mfma32<T>(rdK.template read<t>(cK, 32 * blk), qreg[t], s[blk]);
+      });
+    } else {
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) s[blk] = mfma32<T>(kop[NBLK * t + blk], qreg[t], s[blk]);
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) s[blk] = mfma32<T>(kop[NBLK * t + blk], qreg[t], s[blk]);
+    }
 
     // keep bytes (dropout): runs of 4 keys
     uint32_t kw[8];
@@ -278,12 +300,15 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     }
 
     // all V^T operands of this tile, requested before the exponentials
-    u32x4 vop[2 * NBLK * DB];
+    // (LEAN: each slice's, at the slice)
+    u32x4 vop[LEAN ? DB : 2 * NBLK * DB];
+    if constexpr (!LEAN) {
 #pragma unroll
-    for (int tt = 0; tt < 2 * NBLK; ++tt)
-      static_for<DB>([&](auto db) __attribute__((always_inline)) {
-        vop[tt * DB + db] = rdV.template read<32 * db>(cV, 16 * tt);
-      });
+      for (int tt = 0; tt < 2 * NBLK; ++tt)
+        static_for<DB>([&](auto db) __attribute__((always_inline)) {
+          vop[tt * DB + db] = rdV.template read<32 * db>(cV, 16 * tt);
+        });
+    }
 
     const float m_new = fmaxf(m_run, mrow);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + TAU) != 0) {
@@ -319,8 +344,16 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[tt][e] = pack2<T>(p[2 * e], p[2 * e + 1]);
       // O^T += V^T P^T for this slice
+      if constexpr (LEAN) {
+        static_for<DB>([&](auto db) __attribute__((always_inline)) {
+          vop[db] = rdV.template read<32 * db>(cV, 16 * tt);
+        });
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb[tt], oacc[db]);
+        for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[db], pb[tt], oacc[db]);
+      } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = mfma32<T>(vop[tt * DB + db], pb[tt], oacc[db]);
+      }
     });
     l_run += psum;
 
