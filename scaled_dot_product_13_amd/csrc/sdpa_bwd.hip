@@ -100,7 +100,10 @@ __global__ void __launch_bounds__(256) bwd_pre(const BwdArgs a, int dv) {
 // only half of the stationary state (K and dV, or V and dK) in registers.
 template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
-  constexpr int BC = 128, BQ = 32, NSET = 3;
+  // QBLK 32-row query blocks per trip (two where the LDS holds them), so
+  // that each barrier and P hand-over covers QBLK blocks' products
+  constexpr int QBLK = (!BIAS && !DROP && DQK <= 128 && DV <= 128) ? 2 : 1;
+  constexpr int BC = 128, BQ = 32 * QBLK, NSET = 3;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
   constexpr bool BIAS_LDS = BIAS && DQK <= SDPA_DKDV_BIAS_LDS_MAXD;
   // Query-side tiles are triple-buffered: role A reads set i % 3, role B
@@ -109,9 +112,9 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) T sO[NSET][BQ * DV];
   __shared__ __attribute__((aligned(1024))) T sB[BIAS_LDS ? NSET : 1][BIAS_LDS ? BQ * BC : 64];
   __shared__ __attribute__((aligned(256))) float sL[NSET][BQ], sD[NSET][BQ];
-  // P from role A to role B in the io type: [slot][key block][2 groups of 8
-  // elements][lane]
-  __shared__ __attribute__((aligned(1024))) u32x4 sP[2][4][2][64];
+  // P from role A to role B in the io type: [slot][key block][query block]
+  // [2 groups of 8 elements][lane]
+  __shared__ __attribute__((aligned(1024))) u32x4 sP[2][4][QBLK][2][64];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
@@ -228,9 +231,13 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   auto tile_active = [&](Item it) __attribute__((always_inline)) {
     return wk0 < skv && (!BAND || (wk0 + 31 - it.q0 >= bd.lo && wk0 - (it.q0 + BQ - 1) <= bd.hi));
   };
-  auto tile_needs_mask = [&](Item it) __attribute__((always_inline)) {
-    return (it.q0 + BQ > sq) || (wk0 + 31 >= skv) ||
-           (BAND && !(wk0 - (it.q0 + BQ - 1) >= bd.lo && wk0 + 31 - it.q0 <= bd.hi));
+  // the same for one 32-row block starting at row q0
+  auto block_active = [&](int q0) __attribute__((always_inline)) {
+    return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
+  };
+  auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
+    return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
+           (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
   };
 
   RowReader<DQK, T> rdQ;
@@ -241,14 +248,17 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   rdOt.init(lane);
   rdO.init(lane);
   rdQt.init(lane);
-  // this lane's P slot: 2 x 16 bytes at stride 1 KiB
-  const uint32_t p_lane = lds_addr(&sP[0][kb][0][0]) + 16 * lane;
-  constexpr uint32_t P_SLOT = 4 * 2 * 64 * 16;
+  // this lane's P slot: per query block 2 x 16 bytes at stride 1 KiB
+  const uint32_t p_lane = lds_addr(&sP[0][kb][0][0][0]) + 16 * lane;
+  constexpr uint32_t P_SLOT = 4 * QBLK * 2 * 64 * 16;
 
   // ---- role A: S, P, dV for tile i -----------------------------------------
   auto stepA = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
       __attribute__((always_inline)) {
-    const int q0 = it.q0, h = it.h;
+   static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
+    constexpr int QB2 = decltype(qbc)::value;  // query block within the trip
+    const int q0 = it.q0 + 32 * QB2, h = it.h;
+    if (QBLK > 1 && !block_active(q0)) return;
     const uint32_t bh = (uint32_t)(b * a.H + h);
     const uint16_t* bg = BIAS ? bias_head(h) : nullptr;
     const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sq, skv);
@@ -263,7 +273,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     f32x16 s = f32x16{};
     static_for<KT / KH>([&](auto hf) __attribute__((always_inline)) {
       static_for<KH>([&](auto j) __attribute__((always_inline)) {
-        qop[j] = vQ.template read<hf * KH + j>(0);
+        qop[j] = vQ.template read<hf * KH + j>(32 * QB2);
       });
 #pragma unroll
       for (int j = 0; j < KH; ++j) s = mfma32<T>(qop[j], reg[hf * KH + j], s);
@@ -275,7 +285,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     auto read_oop = [&]() __attribute__((always_inline)) {
       static_for<VB>([&](auto vb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) oop[tt * VB + vb] = vOt.template read<32 * vb>(16 * tt);
+        for (int tt = 0; tt < 2; ++tt) oop[tt * VB + vb] = vOt.template read<32 * vb>(16 * tt + 32 * QB2);
       });
     };
     if constexpr (EARLY_O) read_oop();
@@ -287,7 +297,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
       quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
     }
-    const float* cL = sL[set];
+    const float* cL = sL[set] + 32 * QB2;
     const T* cB = sB[BIAS_LDS ? set : 0];
     float pv[16];
 #pragma unroll
@@ -299,7 +309,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         const int r = 8 * hh + e;
         float x = -(e < 4 ? L0[e] : L1[e - 4]);  // exponent = c s + log2e bias - LSE log2e
         if (BIAS) {
-          const int ql = lb + e, qr = q0 + ql;
+          const int ql = 32 * QB2 + lb + e, qr = q0 + lb + e;
           float bval = 0.f;
           if (alibi)
             bval = alibi_at(at, kvr, qr);
@@ -312,7 +322,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, x));
       }
     }
-    if (tile_needs_mask(it)) {
+    if (block_needs_mask(q0)) {
       keep_branch();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -346,7 +356,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
             pb[tt][e] = wd;
           }
         }
-      const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
+      const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT + 2048 * QB2;
 #pragma unroll
       for (int j = 0; j < 2; ++j) *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(pa + 1024 * j) = ph[j];
     }
@@ -356,12 +366,17 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma32<T>(oop[tt * VB + vb], pb[tt], acc[vb]);
+   });
   };
 
   // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
   auto stepB = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
       __attribute__((always_inline)) {
-    const int q0 = it.q0;
+   static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
+    constexpr int QB2 = decltype(qbc)::value;
+    static_assert(QBLK == 1 || !BIAS, "a skipped block would leave its dBias rows unwritten");
+    const int q0 = it.q0 + 32 * QB2;
+    if (QBLK > 1 && !block_active(q0)) return;
     uint16_t* dbg = want_dbias ? dbias_head(it.h) : nullptr;
     const auto vO = rdO.view(sO[set]);
     const auto vQt = rdQt.view(sQ[set]);
@@ -371,7 +386,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     f32x16 dp = f32x16{};
     static_for<VT / VH>([&](auto hf) __attribute__((always_inline)) {
       static_for<VH>([&](auto j) __attribute__((always_inline)) {
-        oop[j] = vO.template read<hf * VH + j>(0);
+        oop[j] = vO.template read<hf * VH + j>(32 * QB2);
       });
 #pragma unroll
       for (int j = 0; j < VH; ++j) dp = mfma32<T>(oop[j], reg[hf * VH + j], dp);
@@ -381,13 +396,13 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     u32x4 qtop[2 * QH];
     static_for<QH>([&](auto qb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + qb] = vQt.template read<32 * qb>(16 * tt);
+      for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + qb] = vQt.template read<32 * qb>(16 * tt + 32 * QB2);
     });
-    const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT;
+    const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT + 2048 * QB2;
     u32x4 pw[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) pw[j] = lds_load16(pa + 1024 * j);
-    const float* cD = sD[set];
+    const float* cD = sD[set] + 32 * QB2;
     u32x4 dsb[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -425,13 +440,14 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     if constexpr (QH < QB) {
       static_for<QB - QH>([&](auto j) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + j] = vQt.template read<32 * (QH + j)>(16 * tt);
+        for (int tt = 0; tt < 2; ++tt) qtop[tt * QH + j] = vQt.template read<32 * (QH + j)>(16 * tt + 32 * QB2);
       });
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int j = 0; j < QB - QH; ++j) acc[QH + j] = mfma32<T>(qtop[tt * QH + j], dsb[tt], acc[QH + j]);
     }
+   });
   };
 
   const Item first{hk * G, q_begin};
