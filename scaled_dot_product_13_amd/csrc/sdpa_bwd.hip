@@ -21,6 +21,7 @@
 // reduction with no workspace, no atomics and no inter-workgroup waiting;
 // CK instead writes one fp32 dQ slice per key tile and sums the slices in
 // FmhaBwdConvertQGradKernel, and oneDNN adds fp32 dQ atomically.
+#include <atomic>
 #include <type_traits>
 
 #include "sdpa_kcommon.h"
@@ -104,6 +105,12 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   // that each barrier and P hand-over covers QBLK blocks' products
   constexpr int QBLK = (!BIAS && !DROP && DQK <= 128 && DV <= 128) ? 2 : 1;
   constexpr int BC = 128, BQ = 32 * QBLK, NSET = 3;
+  // STREAM: a workgroup may take several units (the launch caps the grid at
+  // the compute units), and role A's waves load every query-side tile.  The
+  // bias and dropout instances, whose role A has the longer element-wise
+  // work, run one unit per workgroup with all eight waves sharing the loads
+  // (measured faster for them).
+  constexpr bool STREAM = !BIAS && !DROP;
   constexpr int KT = DQK / 16, VT = DV / 16, QB = DQK / 32, VB = DV / 32;
   constexpr bool BIAS_LDS = BIAS && DQK <= SDPA_DKDV_BIAS_LDS_MAXD;
   // Query-side tiles are triple-buffered: role A reads set i % 3, role B
@@ -120,89 +127,111 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   const int w = wave_id();
   const int kb = w & 3;
   const bool roleA = w < 4;
-  // one workgroup per (batch, key/value head, key tile); it accumulates dK,
-  // dV over the query tiles of every query head of the head's group
   const int G = a.G;
-  const WorkItem wi = xcd_work((a.seq.s_kv + BC - 1) / BC, a.H / G, a.B, SDPA_DKDV_HEAD_GROUP, a.seq.cu_q != nullptr);
-  if (!wi.valid) return;
-  const int b = wi.b, hk = wi.h;
-  const SeqPos sp = resolve_seq(a.seq, b);
-  const int sq = sp.sq, skv = sp.skv;
-  const int kv0 = wi.tile * BC;  // top-left causal: key tile 0 has the most query tiles
-  if (kv0 >= skv) return;
-  const Band bd = seq_band(a.band_br, a.band_lo, a.band_hi, sq, skv);
-
-  const T* kg = base_ptr<T>(a.k, a.sk_, sp, hk, false);
-  const T* vg = base_ptr<T>(a.v, a.sv_, sp, hk, false);
-  // per query head: its bias / dBias rows
-  auto bias_head = [&](int h) __attribute__((always_inline)) {
-    return (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
-  };
-  auto dbias_head = [&](int h) __attribute__((always_inline)) {
-    return (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
-  };
   const bool want_dbias = BIAS && a.dbias != nullptr;
   const bool alibi = BIAS && a.alibi != nullptr;  // computed in place of the bias tensor
-
-  const int wk0 = kv0 + 32 * kb;  // this wave's first key
-  const int kvr = wk0 + l32;      // this lane's key
-  const bool kv_ok = kvr < skv;
   DropKey dk{};
   if (DROP) dk = drop_key(a.drop);
   const float rescale = DROP ? a.drop.rescale : 1.f;
   const float c = a.scale_log2;
+  // per query head: its bias / dBias rows
+  auto bias_head = [&](int b, int h) __attribute__((always_inline)) {
+    return (const uint16_t*)a.bias + (int64_t)b * a.sb_.b + (int64_t)h * a.sb_.h;
+  };
+  auto dbias_head = [&](int b, int h) __attribute__((always_inline)) {
+    return (uint16_t*)a.dbias + (int64_t)b * a.sdb_.b + (int64_t)h * a.sdb_.h;
+  };
 
-  // banded: only rows [kv0 - hi, kv_last - lo] see any of these keys; the
-  // query tiles run over them from a tile boundary
-  int q_begin = 0, q_end = sq;
-  if (BAND) {
-    const int64_t kv_last = min(kv0 + BC, skv) - 1;
-    const int64_t r_lo = max((int64_t)0, (int64_t)kv0 - bd.hi);
-    const int64_t r_hi = min((int64_t)sq, kv_last - bd.lo + 1);
-    q_begin = r_lo < r_hi ? (int)(r_lo / BQ) * BQ : 0;
-    q_end = r_lo < r_hi ? (int)r_hi : 0;
-  }
-  const int nq = q_end > q_begin ? (q_end - q_begin + BQ - 1) / BQ : 0;
-  // work items: item i is query tile i % nq of query head hk*G + i / nq,
-  // i < G * nq; the trip loop steps them incrementally (no divisions)
-  const int n_items = G * nq;
+  // ---- work units ----------------------------------------------------------
+  // A unit is one (batch, key/value head, 128-key tile): it accumulates dK
+  // and dV over the query tiles of every query head of the head's group.
+  // With fewer workgroups than units, workgroup p = 8 r + x takes the units
+  // of XCD x at positions r, 2R-1-r, 2R+r, 4R-1-r, ... (R workgroups per
+  // XCD; every other round reversed, which evens out the heaviest-first
+  // order) and streams their query tiles back to back: the trip pipeline
+  // runs across unit boundaries, and each role loads the next unit's
+  // stationary operands while the other role finishes the previous one.
+  const int ntiles = (a.seq.s_kv + BC - 1) / BC;
+  const int HG = a.H / G;
+  const int R = (int)(gridDim.x >> 3), xg = (int)(blockIdx.x & 7), rg = (int)(blockIdx.x >> 3);
+  const int npos = (int)(((int64_t)a.B * HG + 7) / 8) * ntiles;
+  // (only the scalars the trip loop needs: the sequence's token offsets are
+  // looked up again where pointers are formed)
+  struct Unit {
+    Band bd;
+    int b, hk, kv0, sq, skv, q_begin, nq;
+    int n;  // items: G nq query tiles (one empty item when nq = 0); 0 past the keys
+  };
+  auto get_unit = [&](int k, Unit& u) __attribute__((always_inline)) -> bool {
+    const int pos = k * R + ((k & 1) ? R - 1 - rg : rg);
+    if (pos >= npos) return false;
+    const WorkItem wi = xcd_work_at(8 * pos + xg, ntiles, HG, a.B, SDPA_DKDV_HEAD_GROUP, a.seq.cu_q != nullptr);
+    if (!wi.valid) return false;
+    u.b = wi.b;
+    u.hk = wi.h;
+    u.kv0 = wi.tile * BC;
+    const SeqPos sp = resolve_seq(a.seq, u.b);
+    u.sq = sp.sq;
+    u.skv = sp.skv;
+    u.bd = seq_band(a.band_br, a.band_lo, a.band_hi, u.sq, u.skv);
+    // banded: only rows [kv0 - hi, kv_last - lo] see any of these keys; the
+    // query tiles run over them from a tile boundary
+    int q_begin = 0, q_end = u.sq;
+    if (BAND) {
+      const int64_t kv_last = min(u.kv0 + BC, u.skv) - 1;
+      const int64_t r_lo = max((int64_t)0, (int64_t)u.kv0 - u.bd.hi);
+      const int64_t r_hi = min((int64_t)u.sq, kv_last - u.bd.lo + 1);
+      q_begin = r_lo < r_hi ? (int)(r_lo / BQ) * BQ : 0;
+      q_end = r_lo < r_hi ? (int)r_hi : 0;
+    }
+    u.q_begin = q_begin;
+    u.nq = q_end > q_begin ? (q_end - q_begin + BQ - 1) / BQ : 0;
+    u.n = u.kv0 < u.skv ? max(G * u.nq, 1) : 0;
+    return true;
+  };
+  // the first unit at index >= k that has keys here (its index, or -1)
+  auto find_unit = [&](int k, Unit& u) __attribute__((always_inline)) -> int {
+    for (;; ++k) {
+      if (!get_unit(k, u)) return -1;
+      if (u.n > 0) return k;
+    }
+  };
+  // an item: query tile q0 of query head h; item j of a unit is query tile
+  // j % nq of head hk G + j / nq
   struct Item {
     int h, q0;
   };
-  auto next_item = [&](Item it) __attribute__((always_inline)) {
+  auto next_item = [&](const Unit& u, Item it) __attribute__((always_inline)) {
     it.q0 += BQ;
-    if (it.q0 >= q_begin + nq * BQ) {
-      it.q0 = q_begin;
+    if (it.q0 >= u.q_begin + u.nq * BQ) {
+      it.q0 = u.q_begin;
       ++it.h;
     }
     return it;
   };
-  if (BAND && want_dbias && !roleA && kv_ok) {
-    // dBias is zero wherever the mask hides the key: the rows outside the
-    // query tiles
-    const int z_end = min(q_begin, sq), z_begin = min(q_begin + nq * BQ, sq);
-    for (int j = 0; j < G; ++j) {
-      uint16_t* dbg = dbias_head(hk * G + j);
-      for (int i = g; i < z_end; i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
-      for (int i = z_begin + g; i < sq; i += 2) dbg[(int64_t)i * a.sdb_.s + kvr] = 0;
-    }
-  }
 
   // bias tiles come through LDS when the whole 32 x 128 tile is in range and
   // its rows are 16-byte aligned; otherwise each lane reads its elements.
-  const bool bias_lds = BIAS_LDS && a.bias_vec && kv0 + BC <= skv;
-  constexpr int NWQ = (BQ * DQK / 8) % 512 == 0 ? 8 : 4;
-  constexpr int NWO = (BQ * DV / 8) % 512 == 0 ? 8 : 4;
+  auto bias_lds_of = [&](const Unit& u) __attribute__((always_inline)) {
+    return BIAS_LDS && a.bias_vec && u.kv0 + BC <= u.skv;
+  };
+  // waves sharing each tile's loads, and the two that load LSE and D
+  constexpr int NWQ = STREAM ? 4 : ((BQ * DQK / 8) % 512 == 0 ? 8 : 4);
+  constexpr int NWO = STREAM ? 4 : ((BQ * DV / 8) % 512 == 0 ? 8 : 4);
+  constexpr int NWB = STREAM ? 4 : 8;
+  constexpr int WL = STREAM ? 2 : 6, WD = WL + 1;
   TileLoader<DQK, BQ, T, NWQ> ldQ;
   TileLoader<DV, BQ, T, NWO> ldO;
-  TileLoader<BC, BQ, T, 8> ldB;
-  // the loaders' per-lane offsets depend only on the row strides; the head
-  // of each item moves their base
-  if (w < NWQ) ldQ.init(base_ptr<T>(a.q, a.sq_, sp, hk * G, true), a.sq_.s, w, lane);
-  if (w < NWO) ldO.init(base_ptr<T>(a.dout, a.sdo_, sp, hk * G, true), a.sdo_.s, w, lane);
-  if (BIAS_LDS && bias_lds) ldB.init((const T*)(bias_head(hk * G) + kv0), a.sb_.s, w, lane);
-  auto issue = [&](int set, Item it) __attribute__((always_inline)) {
-    const int q0 = it.q0, h = it.h;
+  TileLoader<BC, BQ, T, NWB> ldB;
+  // the loaders' per-lane offsets depend only on the row strides; each item
+  // moves their base
+  if (w < NWQ) ldQ.init((const T*)a.q, a.sq_.s, w, lane);
+  if (w < NWO) ldO.init((const T*)a.dout, a.sdo_.s, w, lane);
+  if (BIAS_LDS && w < NWB) ldB.init((const T*)a.bias, a.sb_.s, w, lane);
+  // (sp: the unit's sequence, resolve_seq(a.seq, u.b))
+  auto issue = [&](int set, const Unit& u, const SeqPos& sp, Item it) __attribute__((always_inline)) {
+    if (u.nq == 0) return;  // the empty item of a unit no query row sees
+    const int q0 = it.q0, h = it.h, sq = u.sq;
     if (w < NWQ) {
       ldQ.g = (const char*)base_ptr<T>(a.q, a.sq_, sp, h, true);
       ldQ.load(sQ[set], q0, sq, w, lane);
@@ -211,33 +240,27 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       ldO.g = (const char*)base_ptr<T>(a.dout, a.sdo_, sp, h, true);
       ldO.load(sO[set], q0, sq, w, lane);
     }
-    if (BIAS_LDS && bias_lds) {
-      ldB.g = (const char*)(bias_head(h) + kv0);
+    if (BIAS_LDS && w < NWB && bias_lds_of(u)) {
+      ldB.g = (const char*)(bias_head(u.b, h) + u.kv0);
       ldB.load(sB[set], q0, sq, w, lane);
     }
-    // the 32 LSE*log2(e) (wave 6) and D (wave 7) values, one row per lane,
+    // the BQ LSE*log2(e) (wave WL) and D (wave WD) values, one row per lane,
     // rows clamped to the sequence
-    if (w >= 6 && lane < BQ) {
+    if ((w == WL || w == WD) && lane < BQ) {
       int r = q0 + lane;
       r = r < sq ? r : sq - 1;
-      const int64_t st_base = row_stat_base(a.seq, sp, b, h, a.H, (int64_t)a.B * a.seq.s_q);
-      const float* src = (w == 6 ? a.lse2 : a.dvec) + st_base + r;
-      float* dst = w == 6 ? sL[set] : sD[set];
+      const int64_t st_base = row_stat_base(a.seq, sp, u.b, h, a.H, (int64_t)a.B * a.seq.s_q);
+      const float* src = (w == WL ? a.lse2 : a.dvec) + st_base + r;
+      float* dst = w == WL ? sL[set] : sD[set];
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 4, 0, 0);
     }
   };
-  // key - row over this wave's 32 keys and the tile's rows spans
+  // key - row over this wave's 32 keys and the item's rows spans
   // [wk0 - (q0 + BQ - 1), wk0 + 31 - q0]
-  auto tile_active = [&](Item it) __attribute__((always_inline)) {
-    return wk0 < skv && (!BAND || (wk0 + 31 - it.q0 >= bd.lo && wk0 - (it.q0 + BQ - 1) <= bd.hi));
-  };
-  // the same for one 32-row block starting at row q0
-  auto block_active = [&](int q0) __attribute__((always_inline)) {
-    return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
-  };
-  auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
-    return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
-           (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
+  auto tile_active = [&](const Unit& u, Item it) __attribute__((always_inline)) {
+    const int wk0 = u.kv0 + 32 * kb;
+    return u.nq > 0 && wk0 < u.skv &&
+           (!BAND || (wk0 + 31 - it.q0 >= u.bd.lo && wk0 - (it.q0 + BQ - 1) <= u.bd.hi));
   };
 
   RowReader<DQK, T> rdQ;
@@ -253,14 +276,27 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   constexpr uint32_t P_SLOT = 4 * QBLK * 2 * 64 * 16;
 
   // ---- role A: S, P, dV for tile i -----------------------------------------
-  auto stepA = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
+  auto stepA = [&](int i, int set, const Unit& u, Item it, const u32x4* reg, f32x16* acc)
       __attribute__((always_inline)) {
+    const int b = u.b, sq = u.sq, skv = u.skv;
+    const Band bd = u.bd;
+    const int wk0 = u.kv0 + 32 * kb, kvr = wk0 + l32;
+    const bool kv_ok = kvr < skv;
+    // the same for one 32-row block starting at row q0
+    auto block_active = [&](int q0) __attribute__((always_inline)) {
+      return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
+    };
+    auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
+      return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
+             (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
+    };
+    const bool bias_lds = bias_lds_of(u);
    static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
     constexpr int QB2 = decltype(qbc)::value;  // query block within the trip
     const int q0 = it.q0 + 32 * QB2, h = it.h;
     if (QBLK > 1 && !block_active(q0)) return;
     const uint32_t bh = (uint32_t)(b * a.H + h);
-    const uint16_t* bg = BIAS ? bias_head(h) : nullptr;
+    const uint16_t* bg = BIAS ? bias_head(b, h) : nullptr;
     const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sq, skv);
     const auto vQ = rdQ.view(sQ[set]);
     const auto vOt = rdOt.view(sO[set]);
@@ -370,14 +406,26 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   };
 
   // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
-  auto stepB = [&](int i, int set, Item it, const u32x4* reg, f32x16* acc)
+  auto stepB = [&](int i, int set, const Unit& u, Item it, const u32x4* reg, f32x16* acc)
       __attribute__((always_inline)) {
+    const int b = u.b, sq = u.sq, skv = u.skv;
+    const Band bd = u.bd;
+    const int wk0 = u.kv0 + 32 * kb, kvr = wk0 + l32;
+    const bool kv_ok = kvr < skv;
+    // the same for one 32-row block starting at row q0
+    auto block_active = [&](int q0) __attribute__((always_inline)) {
+      return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
+    };
+    auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
+      return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
+             (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
+    };
    static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
     constexpr int QB2 = decltype(qbc)::value;
     static_assert(QBLK == 1 || !BIAS, "a skipped block would leave its dBias rows unwritten");
     const int q0 = it.q0 + 32 * QB2;
     if (QBLK > 1 && !block_active(q0)) return;
-    uint16_t* dbg = want_dbias ? dbias_head(it.h) : nullptr;
+    uint16_t* dbg = want_dbias ? dbias_head(b, it.h) : nullptr;
     const auto vO = rdO.view(sO[set]);
     const auto vQt = rdQt.view(sQ[set]);
     // (in halves when the dK accumulator is large, to bound registers)
@@ -450,55 +498,43 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
    });
   };
 
-  const Item first{hk * G, q_begin};
-  if (n_items > 0) issue(0, first);
   // Each role runs its own copy of the trip loop, so its stationary operands
   // and accumulators are sized for it alone; both copies meet the same
-  // barriers.  Trip i: role A takes tile i, role B tile i - 1.
+  // barriers.  Trip i: role A takes item i (and loads item i + 1), role B
+  // item i - 1; over this workgroup's N items both make N + 1 trips.
   auto run = [&](auto is_a) __attribute__((always_inline)) {
     constexpr bool IS_A = decltype(is_a)::value;
     constexpr int NR = IS_A ? KT : VT, NA = IS_A ? VB : QB;
     u32x4 reg[NR];  // K^T (role A) or V^T (role B) as B operands
-    {
-      const T* src = IS_A ? kg + (int64_t)kvr * a.sk_.s : vg + (int64_t)kvr * a.sv_.s;
+    f32x16 acc[NA];  // dV^T (role A) or dK^T (role B), one key per lane
+    // entering a unit: its stationary operands, a zeroed accumulator and
+    // (role B, banded dBias) zeros in the rows no query tile of it covers
+    auto enter = [&](const Unit& u, const SeqPos& sp) __attribute__((always_inline)) {
+      const int kvr = u.kv0 + 32 * kb + l32;
+      const bool kv_ok = kvr < u.skv;
+      const T* src = IS_A ? base_ptr<T>(a.k, a.sk_, sp, u.hk, false) + (int64_t)kvr * a.sk_.s
+                          : base_ptr<T>(a.v, a.sv_, sp, u.hk, false) + (int64_t)kvr * a.sv_.s;
 #pragma unroll
       for (int t = 0; t < NR; ++t)
         reg[t] = kv_ok ? *(const u32x4*)(src + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
-    }
-    f32x16 acc[NA];  // dV^T (role A) or dK^T (role B), one key per lane
 #pragma unroll
-    for (int j = 0; j < NA; ++j) acc[j] = f32x16{};
-
-    // items i - 1, i, i + 1 and their buffer sets, stepped each trip
-    Item prev{}, cur = first, nxt = next_item(first);
-    int set_prev = NSET - 1, set_cur = 0, set_nxt = 1;
-    for (int i = 0; i <= n_items; ++i) {
-      wait_all();
-      __syncthreads();  // item i landed; P(i-1) written; set (i+1)%3 free
-      if (i + 1 < n_items) issue(set_nxt, nxt);
-      if constexpr (IS_A) {
-        if (i < n_items && tile_active(cur)) stepA(i, set_cur, cur, reg, acc);
-      } else if (i >= 1) {
-        if (tile_active(prev)) {
-          stepB(i - 1, set_prev, prev, reg, acc);
-        } else if (BAND && want_dbias && kv_ok) {
-          // the whole tile is hidden from my key
-          uint16_t* dbg = dbias_head(prev.h);
-          for (int r = prev.q0 + g; r < min(prev.q0 + BQ, sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+      for (int j = 0; j < NA; ++j) acc[j] = f32x16{};
+      if (!IS_A && BAND && want_dbias && kv_ok) {
+        const int sq = u.sq;
+        const int z_end = min(u.q_begin, sq), z_begin = min(u.q_begin + u.nq * BQ, sq);
+        for (int jh = 0; jh < G; ++jh) {
+          uint16_t* dbg = dbias_head(u.b, u.hk * G + jh);
+          for (int r = g; r < z_end; r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+          for (int r = z_begin + g; r < sq; r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
         }
       }
-      prev = cur;
-      cur = nxt;
-      nxt = next_item(nxt);
-      set_prev = set_cur;
-      set_cur = set_nxt;
-      set_nxt = set_nxt == NSET - 1 ? 0 : set_nxt + 1;
-    }
-
-    // epilogue: dV = rescale * dV^T acc (role A), dK = scale * dK^T acc (role B)
-    if (kv_ok) {
-      T* dst = IS_A ? base_ptr_mut<T>(a.dv, a.sdv_, sp, hk, false) + (int64_t)kvr * a.sdv_.s
-                    : base_ptr_mut<T>(a.dk, a.sdk_, sp, hk, false) + (int64_t)kvr * a.sdk_.s;
+    };
+    // leaving a unit: dV = rescale * dV^T acc (role A), dK = scale * dK^T acc (role B)
+    auto leave = [&](const Unit& u, const SeqPos& sp) __attribute__((always_inline)) {
+      const int kvr = u.kv0 + 32 * kb + l32;
+      if (kvr >= u.skv) return;
+      T* dst = IS_A ? base_ptr_mut<T>(a.dv, a.sdv_, sp, u.hk, false) + (int64_t)kvr * a.sdv_.s
+                    : base_ptr_mut<T>(a.dk, a.sdk_, sp, u.hk, false) + (int64_t)kvr * a.sdk_.s;
       const float f = IS_A ? rescale : a.scale;
 #pragma unroll
       for (int db = 0; db < NA; ++db) {
@@ -510,6 +546,108 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
           v2[1] = pack2<T>(acc[db][4 * rr + 2] * f, acc[db][4 * rr + 3] * f);
           *(u32x2*)(dst + d) = v2;
         }
+      }
+    };
+
+    int set_prev = NSET - 1, set_cur = 0, set_nxt = 1;
+    auto rotate = [&]() __attribute__((always_inline)) {
+      set_prev = set_cur;
+      set_cur = set_nxt;
+      set_nxt = set_nxt == NSET - 1 ? 0 : set_nxt + 1;
+    };
+    Unit u;
+    if constexpr (!STREAM) {
+      // one unit per workgroup (the launch gives each unit its own): trip i
+      // loads item i + 1 (all eight waves), role A takes item i, role B i - 1
+      if (find_unit(0, u) != 0) return;  // no keys of this tile here
+      const SeqPos sp = resolve_seq(a.seq, u.b);
+      enter(u, sp);
+      const int n = u.n;
+      Item prev{}, cur{u.hk * G, u.q_begin}, nxt = next_item(u, cur);
+      issue(0, u, sp, cur);
+      for (int i = 0; i <= n; ++i) {
+        wait_all();
+        __syncthreads();  // item i landed; P(i-1) written; set (i+1)%3 free
+        if (i + 1 < n) issue(set_nxt, u, sp, nxt);
+        if constexpr (IS_A) {
+          if (i < n && tile_active(u, cur)) stepA(i, set_cur, u, cur, reg, acc);
+        } else if (i >= 1) {
+          if (tile_active(u, prev)) {
+            stepB(i - 1, set_prev, u, prev, reg, acc);
+          } else if (BAND && want_dbias && u.nq > 0) {
+            // the whole item is hidden from my key
+            const int kvr = u.kv0 + 32 * kb + l32;
+            if (kvr < u.skv) {
+              uint16_t* dbg = dbias_head(u.b, prev.h);
+              for (int r = prev.q0 + g; r < min(prev.q0 + BQ, u.sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+            }
+          }
+        }
+        prev = cur;
+        cur = nxt;
+        nxt = next_item(u, nxt);
+        rotate();
+      }
+      leave(u, sp);
+    } else {
+      // several units per workgroup, streamed: role A loads every tile; at a
+      // unit's last item it finds the next unit and loads that unit's first
+      int k = find_unit(0, u);
+      SeqPos sp = resolve_seq(a.seq, k >= 0 ? u.b : 0);
+      if (IS_A && k >= 0) issue(0, u, sp, Item{u.hk * G, u.q_begin});
+      if (!IS_A) {
+        wait_all();
+        __syncthreads();  // trip 0: role B has no item yet
+        rotate();
+      }
+      int gi = 0;  // this role's item number
+      while (k >= 0) {
+        Unit un;  // role A: the next unit
+        SeqPos spn;
+        int kn = -1;
+        enter(u, sp);
+        Item it{u.hk * G, u.q_begin};
+        for (int j = 0; j < u.n; ++j, ++gi) {
+          wait_all();
+          __syncthreads();  // item gi landed; P(gi-1) written; set (gi+1)%3 free
+          if constexpr (IS_A) {
+            if (j + 1 < u.n) {
+              issue(set_nxt, u, sp, next_item(u, it));
+            } else {
+              kn = find_unit(k + 1, un);
+              if (kn >= 0) {
+                spn = resolve_seq(a.seq, un.b);
+                issue(set_nxt, un, spn, Item{un.hk * G, un.q_begin});
+              }
+            }
+          }
+          if (tile_active(u, it)) {
+            if constexpr (IS_A) stepA(gi, set_cur, u, it, reg, acc);
+            else stepB(gi, set_prev, u, it, reg, acc);
+          } else if (!IS_A && BAND && want_dbias && u.nq > 0) {
+            // the whole item is hidden from my key
+            const int kvr = u.kv0 + 32 * kb + l32;
+            if (kvr < u.skv) {
+              uint16_t* dbg = dbias_head(u.b, it.h);
+              for (int r = it.q0 + g; r < min(it.q0 + BQ, u.sq); r += 2) dbg[(int64_t)r * a.sdb_.s + kvr] = 0;
+            }
+          }
+          it = next_item(u, it);
+          rotate();
+        }
+        leave(u, sp);
+        if constexpr (IS_A) {
+          k = kn;
+          u = un;
+          sp = spn;
+        } else {
+          k = find_unit(k + 1, u);
+          if (k >= 0) sp = resolve_seq(a.seq, u.b);
+        }
+      }
+      if (IS_A) {
+        wait_all();
+        __syncthreads();  // the last trip: role B's last item
       }
     }
   };
@@ -961,14 +1099,34 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
   if (!causal && bias && drop) LAUNCH(false, true, true)     \
   if (causal && bias && drop) LAUNCH(true, true, true)
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {
+  // one workgroup per compute unit (a multiple of 8, one per XCD in turn),
+  // each streaming its share of the (batch, head, key tile) units
   dim3 grid = xcd_grid((a.seq.s_kv + 127) / 128, a.H / a.G, a.B), block(512);
+  // (the bias and dropout instances take one unit per workgroup, and so do
+  // packed variable-length batches, whose units differ too much in size for
+  // a fixed split: no cap)
+  const unsigned cap = (unsigned)(device_cus() / 8 * 8);
+  if (!bias && !drop && a.seq.cu_q == nullptr && cap > 0 && grid.x > cap) grid.x = cap;
 #define L(C, BI, DR)                                                                         \
   {                                                                                          \
     hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a);           \
     log_launch("dkdv_mfma", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, \
-               C, BI, DR, "128 keys (8 waves, 2 roles) x 32-row query tiles, 3 LDS sets", grid, block); \
+               C, BI, DR, "128-key units (8 waves, 2 roles) streamed per workgroup, 32/64-row query tiles, 3 LDS sets", grid, block); \
     return hipGetLastError();                                                                \
   }
   SDPA_FLAG_SWITCH(L)

@@ -78,9 +78,11 @@ struct WorkItem {
   int b, h, tile;
   bool valid;
 };
-__device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B, int G, bool hmajor = false) {
+// the item of position `id` of that grid (id = blockIdx.x, or a position a
+// persistent workgroup takes on)
+__device__ __forceinline__ WorkItem xcd_work_at(int id, int ntiles, int H, int B, int G, bool hmajor) {
   const int BH = B * H;
-  const int x = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  const int x = id & 7, pos = id >> 3;
   const int h_lo = (int)((int64_t)x * BH / 8);
   const int nh = (int)((int64_t)(x + 1) * BH / 8) - h_lo;  // heads owned by XCD x
   WorkItem wi;
@@ -99,6 +101,9 @@ __device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B, int G, bo
     wi.h = hb - wi.b * H;
   }
   return wi;
+}
+__device__ __forceinline__ WorkItem xcd_work(int ntiles, int H, int B, int G, bool hmajor = false) {
+  return xcd_work_at((int)blockIdx.x, ntiles, H, B, G, hmajor);
 }
 inline dim3 xcd_grid(int ntiles, int H, int B) {
   const long BH = (long)B * H;
