@@ -308,6 +308,17 @@ sdpa_status_t noalloc_stats(void** out) {
 
 namespace sdpa {
 bool log_enabled() { return log_on(); }
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 void log_launch(const char* kernel, IoType t, int dqk, int dv, bool band, bool bias, bool drop,
                 const char* tile, dim3 grid, dim3 block) {
   if (!log_on()) return;

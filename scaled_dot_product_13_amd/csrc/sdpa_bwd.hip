@@ -21,7 +21,6 @@
 // reduction with no workspace, no atomics and no inter-workgroup waiting;
 // CK instead writes one fp32 dQ slice per key tile and sums the slices in
 // FmhaBwdConvertQGradKernel, and oneDNN adds fp32 dQ atomically.
-#include <atomic>
 #include <type_traits>
 
 #include "sdpa_kcommon.h"
@@ -1098,19 +1097,6 @@ hipError_t launch_bwd_pre(IoType t, int dv, const BwdArgs& a, hipStream_t st) {
   if (causal && !bias && drop) LAUNCH(true, false, true)     \
   if (!causal && bias && drop) LAUNCH(false, true, true)     \
   if (causal && bias && drop) LAUNCH(true, true, true)
-
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <typename T, int DQK, int DV>
 static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a, hipStream_t st) {

@@ -63,13 +63,20 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
   // some row's max grows by more than TAU (log2 units); until then the
   // probabilities are exp2(x - m_run) <= 2^TAU, exact in fp32 and bf16.
   constexpr float TAU = 8.f;
+  // STREAM: the launch may give a workgroup several units (plain batch-mode
+  // problems without bias or dropout, whose grid is capped at two
+  // workgroups per compute unit)
+  constexpr bool STREAM = !BIAS && !DROP;
   __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];  // double-buffered tiles
   __shared__ __attribute__((aligned(1024))) T sV[2][BC * DV];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, a.seq.cu_q != nullptr);
+  const bool hmajor = a.seq.cu_q != nullptr;
+
+  // One unit: 128 query rows of one (batch, head).
+  auto unit = [&](const WorkItem wi) __attribute__((always_inline)) {
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest causal tiles first
@@ -400,6 +407,26 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
       a.lse[base + row] = l_row > 0.f ? (m_run + log2f(l_row)) * kLn2 : -INFINITY;
     }
   }
+  };
+
+  if (STREAM) {
+    // The grid may be smaller than the number of units: workgroup p = 8 r + x
+    // takes the units of XCD x at positions r, 2R-1-r, 2R+r, ... (R
+    // workgroups per XCD, every other round reversed to even out the
+    // heaviest-first order), one after another.
+    const int R = (int)(gridDim.x >> 3), xg = (int)(blockIdx.x & 7), rg = (int)(blockIdx.x >> 3);
+    const int npos = (int)(((int64_t)a.B * a.H + 7) / 8) * nqt;
+    for (int k = 0;; ++k) {
+      const int pos = k * R + ((k & 1) ? R - 1 - rg : rg);
+      if (pos >= npos) break;
+      const WorkItem wi = xcd_work_at(8 * pos + xg, nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, hmajor);
+      if (!wi.valid) break;  // (positions only grow)
+      if (k > 0) __syncthreads();  // every wave is done with the last unit's tiles
+      unit(wi);
+    }
+  } else {
+    unit(xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, hmajor));
+  }
 }
 
 // fp32 io: one wavefront per query row, the head dims spread over lanes.
@@ -481,8 +508,15 @@ template <typename T, int DQK, int DV>
 static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const FwdArgs& a,
                                      hipStream_t st) {
   dim3 grid = xcd_grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
+  // the plain instances stream units: as many workgroups as run at once
+  // (their occupancy times the compute units, a multiple of 8)
+  const int cus = device_cus() / 8 * 8;
 #define SDPA_FWD_CASE(C, BI, DR)                                                 \
   if (causal == C && bias == BI && drop == DR) {                                 \
+    if (!BI && !DR && a.seq.cu_q == nullptr && cus > 0) {                        \
+      const unsigned cap = (unsigned)(cus * FwdOcc<DQK, DV, DR, C, BI>::value);  \
+      if (grid.x > cap) grid.x = cap;                                            \
+    }                                                                            \
     hipLaunchKernelGGL((fwd_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); \
     log_launch("fwd_mfma", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, \
                C, BI, DR, "128 query rows (4 waves x 32) x 64-key tiles, 2 LDS buffers", grid, block); \

@@ -117,6 +117,9 @@ constexpr int64_t kDecodeMaxSq = 16;  // thin-query path: s_q <= 16
 // flags), its tile shape and its grid, as oneDNN's SDPA driver prints the
 // configuration it chose.  Host only.
 bool log_enabled();
+// Compute units of the current device (0 if the runtime cannot say); the
+// persistent launches size their grids by it.  Host only.
+int device_cus();
 void log_launch(const char* kernel, IoType t, int dqk, int dv, bool band, bool bias, bool drop,
                 const char* tile, dim3 grid, dim3 block);
 
