@@ -304,6 +304,50 @@ sdpa_status_t noalloc_stats(void** out) {
   return SDPA_OK;
 }
 
+// One of SDPA_FWD_CONFIG / SDPA_BWD_CONFIG: comma-separated key=value with
+// integer values, keys from `keys` (LaunchConfig in sdpa_params.h).
+sdpa_status_t parse_config_env(const char* name, const char* const* keys, int* const* vals, int nk) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return SDPA_OK;
+  const char* c = s;
+  while (*c) {
+    const char* eq = std::strchr(c, '=');
+    const char* comma = std::strchr(c, ',');
+    if (!eq || (comma && comma < eq))
+      return fail(SDPA_ERR_INVALID_ARG, "%s: expected key=value items in \"%s\"", name, s);
+    const size_t klen = (size_t)(eq - c);
+    int idx = -1;
+    for (int i = 0; i < nk; ++i)
+      if (std::strlen(keys[i]) == klen && std::strncmp(keys[i], c, klen) == 0) idx = i;
+    if (idx < 0) return fail(SDPA_ERR_INVALID_ARG, "%s: unknown key \"%.*s\"", name, (int)klen, c);
+    char* end = nullptr;
+    const long v = std::strtol(eq + 1, &end, 10);
+    if (end == eq + 1 || (*end && *end != ',') || v < -1 || v > (1L << 20))
+      return fail(SDPA_ERR_INVALID_ARG, "%s: bad value for %s in \"%s\"", name, keys[idx], s);
+    *vals[idx] = (int)v;
+    c = *end == ',' ? end + 1 : end;
+  }
+  return SDPA_OK;
+}
+
+// The launch configuration: defaults, then the environment overrides,
+// validated (head groups 1 .. 64; workgroup counts -1, 0 or a positive
+// multiple of 8).
+sdpa_status_t launch_config(sdpa::LaunchConfig& cfg) {
+  static const char* const fk[] = {"heads", "wgs"};
+  int* const fv[] = {&cfg.fwd_heads, &cfg.fwd_wgs};
+  if (sdpa_status_t st = parse_config_env("SDPA_FWD_CONFIG", fk, fv, 2); st != SDPA_OK) return st;
+  static const char* const bk[] = {"dq_heads", "dkdv_heads", "dkdv_wgs"};
+  int* const bv[] = {&cfg.dq_heads, &cfg.dkdv_heads, &cfg.dkdv_wgs};
+  if (sdpa_status_t st = parse_config_env("SDPA_BWD_CONFIG", bk, bv, 3); st != SDPA_OK) return st;
+  for (int h : {cfg.fwd_heads, cfg.dq_heads, cfg.dkdv_heads})
+    if (h < 1 || h > 64) return fail(SDPA_ERR_INVALID_ARG, "launch config: head groups must be 1 .. 64");
+  for (int wgs : {cfg.fwd_wgs, cfg.dkdv_wgs})
+    if (wgs > 0 && wgs % 8 != 0)
+      return fail(SDPA_ERR_INVALID_ARG, "launch config: workgroup counts must be multiples of 8");
+  return SDPA_OK;
+}
+
 }  // namespace
 
 namespace sdpa {
@@ -397,6 +441,12 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   a.scale = p->scaling_factor;
   a.scale_log2 = (float)((double)p->scaling_factor * 1.4426950408889634);
   fill_dropout(p, a.drop);
+  {
+    sdpa::LaunchConfig cfg;
+    if ((st = launch_config(cfg)) != SDPA_OK) return st;
+    a.head_group = cfg.fwd_heads;
+    a.grid_cap = cfg.fwd_wgs;
+  }
   if (log_on())
     std::fprintf(stderr, "[sdpa] fwd dtype=%d b=%lld h=%lld s_q=%lld s_kv=%lld d=%lld/%lld causal=%d "
                  "bias=%d p=%g group=%d\n", (int)p->dtype, (long long)p->b, (long long)p->h,
@@ -444,6 +494,11 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
 }
 
 static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
+  sdpa::LaunchConfig cfg;
+  if (sdpa_status_t st = launch_config(cfg); st != SDPA_OK) return st;
+  a.dq_head_group = cfg.dq_heads;
+  a.dkdv_head_group = cfg.dkdv_heads;
+  a.dkdv_grid_cap = cfg.dkdv_wgs;
   a.B = (int32_t)p->b; a.H = (int32_t)p->h; a.G = kv_group(p);
   band_of(p, a.band_br, a.band_lo, a.band_hi);
   fill_alibi(p, a);
@@ -470,7 +525,7 @@ sdpa_status_t sdpa_bwd_preprocess(const sdpa_problem_t* p, const void* o, sdpa_s
   if (p->d_v % (16 / (int)elem_size(p->dtype)) != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "d_v must fill whole 16-byte chunks");
   sdpa::BwdArgs a{};
-  fill_bwd_args(p, a);
+  if (sdpa_status_t fs = fill_bwd_args(p, a); fs != SDPA_OK) return fs;
   a.o = o; a.dout = d_o; a.so_ = to_str(o_s); a.sdo_ = to_str(do_s);
   a.lse = softmax_lse;
   a.dvec = stats;
@@ -524,7 +579,7 @@ sdpa_status_t sdpa_bwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
     return fail(SDPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   sdpa::BwdArgs a{};
-  fill_bwd_args(p, a);
+  if (sdpa_status_t fs = fill_bwd_args(p, a); fs != SDPA_OK) return fs;
   a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o; a.dout = d_o;
   a.lse = softmax_lse;
   a.dvec = (float*)workspace;
@@ -627,7 +682,7 @@ sdpa_status_t sdpa_bwd_dkdv(const sdpa_problem_t* p, const void* q, sdpa_strides
     if ((st = check_tensor(p, dbias, dbias_s, "dbias", false)) != SDPA_OK) return st;
   }
   sdpa::BwdArgs a{};
-  fill_bwd_args(p, a);
+  if (sdpa_status_t fs = fill_bwd_args(p, a); fs != SDPA_OK) return fs;
   a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o;
   a.dvec = (float*)stats; a.lse2 = stats_lse2(p, stats);
   a.dk = dk; a.dv = dv; a.dbias = dbias;
@@ -653,7 +708,7 @@ sdpa_status_t sdpa_bwd_dq(const sdpa_problem_t* p, const void* q, sdpa_strides_t
     return st;
   if ((st = check_tensor(p, dq, dq_s, "dq", p->dtype != SDPA_F32)) != SDPA_OK) return st;
   sdpa::BwdArgs a{};
-  fill_bwd_args(p, a);
+  if (sdpa_status_t fs = fill_bwd_args(p, a); fs != SDPA_OK) return fs;
   a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.dout = d_o;
   a.dvec = (float*)stats; a.lse2 = stats_lse2(p, stats);
   a.dq = dq;
@@ -686,7 +741,7 @@ sdpa_status_t sdpa_bwd_dq_preprocess(const sdpa_problem_t* p, const void* q, sdp
   if ((st = check_tensor(p, dq, dq_s, "dq", true)) != SDPA_OK) return st;
   if (!softmax_lse) return fail(SDPA_ERR_INVALID_ARG, "softmax_lse is null");
   sdpa::BwdArgs a{};
-  fill_bwd_args(p, a);
+  if (sdpa_status_t fs = fill_bwd_args(p, a); fs != SDPA_OK) return fs;
   a.q = q; a.k = k; a.v = v; a.bias = attn_bias; a.o = o; a.dout = d_o;
   a.lse = softmax_lse;
   a.dvec = stats; a.lse2 = stats_lse2(p, stats);

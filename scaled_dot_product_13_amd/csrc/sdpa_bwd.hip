@@ -29,12 +29,6 @@
 #ifndef SDPA_DKDV_BIAS_LDS_MAXD
 #define SDPA_DKDV_BIAS_LDS_MAXD 192
 #endif
-#ifndef SDPA_DKDV_HEAD_GROUP
-#define SDPA_DKDV_HEAD_GROUP 2
-#endif
-#ifndef SDPA_DQ_HEAD_GROUP
-#define SDPA_DQ_HEAD_GROUP 4
-#endif
 
 namespace sdpa {
 
@@ -164,7 +158,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   auto get_unit = [&](int k, Unit& u) __attribute__((always_inline)) -> bool {
     const int pos = k * R + ((k & 1) ? R - 1 - rg : rg);
     if (pos >= npos) return false;
-    const WorkItem wi = xcd_work_at(8 * pos + xg, ntiles, HG, a.B, SDPA_DKDV_HEAD_GROUP, a.seq.cu_q != nullptr);
+    const WorkItem wi = xcd_work_at(8 * pos + xg, ntiles, HG, a.B, a.dkdv_head_group, a.seq.cu_q != nullptr);
     if (!wi.valid) return false;
     u.b = wi.b;
     u.hk = wi.h;
@@ -687,7 +681,7 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int w = wave_id();
   const int nqt = (a.seq.s_q + BR - 1) / BR;
-  const WorkItem wi = xcd_work(nqt, a.H, a.B, SDPA_DQ_HEAD_GROUP, a.seq.cu_q != nullptr);
+  const WorkItem wi = xcd_work(nqt, a.H, a.B, a.dq_head_group, a.seq.cu_q != nullptr);
   if (!wi.valid) return;
   const int b = wi.b, h = wi.h;
   const int mt = BAND ? nqt - 1 - wi.tile : wi.tile;  // heaviest top-left causal tiles first
@@ -1106,8 +1100,10 @@ static hipError_t dkdv_dims(bool causal, bool bias, bool drop, const BwdArgs& a,
   // (the bias and dropout instances take one unit per workgroup, and so do
   // packed variable-length batches, whose units differ too much in size for
   // a fixed split: no cap)
-  const unsigned cap = (unsigned)(device_cus() / 8 * 8);
-  if (!bias && !drop && a.seq.cu_q == nullptr && cap > 0 && grid.x > cap) grid.x = cap;
+  if (!bias && !drop && a.seq.cu_q == nullptr) {
+    const long cap = a.dkdv_grid_cap < 0 ? (long)(device_cus() / 8 * 8) : (long)a.dkdv_grid_cap;
+    if (cap > 0 && (long)grid.x > cap) grid.x = (unsigned)cap;
+  }
 #define L(C, BI, DR)                                                                         \
   {                                                                                          \
     hipLaunchKernelGGL((dkdv_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a);           \

@@ -25,9 +25,6 @@
 #define SDPA_FWD_NBLK 2
 #endif
 // heads whose tiles are interleaved rank-major on one XCD (see xcd_work)
-#ifndef SDPA_FWD_HEAD_GROUP
-#define SDPA_FWD_HEAD_GROUP 4
-#endif
 
 namespace sdpa {
 
@@ -419,13 +416,13 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     for (int k = 0;; ++k) {
       const int pos = k * R + ((k & 1) ? R - 1 - rg : rg);
       if (pos >= npos) break;
-      const WorkItem wi = xcd_work_at(8 * pos + xg, nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, hmajor);
+      const WorkItem wi = xcd_work_at(8 * pos + xg, nqt, a.H, a.B, a.head_group, hmajor);
       if (!wi.valid) break;  // (positions only grow)
       if (k > 0) __syncthreads();  // every wave is done with the last unit's tiles
       unit(wi);
     }
   } else {
-    unit(xcd_work(nqt, a.H, a.B, SDPA_FWD_HEAD_GROUP, hmajor));
+    unit(xcd_work(nqt, a.H, a.B, a.head_group, hmajor));
   }
 }
 
@@ -513,9 +510,10 @@ static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const Fw
   const int cus = device_cus() / 8 * 8;
 #define SDPA_FWD_CASE(C, BI, DR)                                                 \
   if (causal == C && bias == BI && drop == DR) {                                 \
-    if (!BI && !DR && a.seq.cu_q == nullptr && cus > 0) {                        \
-      const unsigned cap = (unsigned)(cus * FwdOcc<DQK, DV, DR, C, BI>::value);  \
-      if (grid.x > cap) grid.x = cap;                                            \
+    if (!BI && !DR && a.seq.cu_q == nullptr) {                                   \
+      const long cap = a.grid_cap < 0 ? (long)cus * FwdOcc<DQK, DV, DR, C, BI>::value \
+                                      : (long)a.grid_cap;                        \
+      if (cap > 0 && (long)grid.x > cap) grid.x = (unsigned)cap;                 \
     }                                                                            \
     hipLaunchKernelGGL((fwd_mfma<T, DQK, DV, C, BI, DR>), grid, block, 0, st, a); \
     log_launch("fwd_mfma", std::is_same<T, __bf16>::value ? IoType::BF16 : IoType::F16, DQK, DV, \

@@ -56,6 +56,10 @@ struct FwdArgs {
   float scale;         // scaling_factor
   float scale_log2;    // scaling_factor * log2(e)
   DropoutArgs drop;
+  // launch configuration (LaunchConfig below): heads per L2 group in the
+  // XCD placement, and the workgroup count of the streamed instances (host)
+  int32_t head_group;
+  int32_t grid_cap;
 };
 
 struct BwdArgs {
@@ -80,6 +84,10 @@ struct BwdArgs {
   SeqInfo seq;
   float scale, scale_log2;
   DropoutArgs drop;
+  // launch configuration (LaunchConfig below): heads per L2 group of the dQ
+  // and dK/dV placements, and the dK/dV workgroup count when streamed (host)
+  int32_t dq_head_group, dkdv_head_group;
+  int32_t dkdv_grid_cap;
 };
 
 // Thin-query forward (split-KV).  Each split of the keys writes a normalised
@@ -116,6 +124,23 @@ constexpr int64_t kDecodeMaxSq = 16;  // thin-query path: s_q <= 16
 // naming the kernel instance (io type, head dims, mask / bias / dropout
 // flags), its tile shape and its grid, as oneDNN's SDPA driver prints the
 // configuration it chose.  Host only.
+// Launch configuration of the tile kernels.  The tile shapes are fixed by
+// the compiled instances; what a launch chooses at run time is the XCD
+// placement's head-group size (heads whose tiles share an L2 at a time) and
+// how many workgroups the streamed instances (batch mode, no bias, no
+// dropout) run: -1 = one per concurrent slot (occupancy x compute units),
+// 0 = one unit per workgroup, n > 0 = n (a multiple of 8).  The defaults
+// can be overridden through the environment, as oneDNN's SDPA_CONFIG and
+// BWD_SDPA_CONFIG override its tile choices:
+//   SDPA_FWD_CONFIG="heads=4,wgs=512"
+//   SDPA_BWD_CONFIG="dq_heads=4,dkdv_heads=2,dkdv_wgs=256"
+// (any subset of the keys).  Results do not depend on these settings.
+struct LaunchConfig {
+  int fwd_heads = 4, fwd_wgs = -1;
+  int dq_heads = 4;
+  int dkdv_heads = 2, dkdv_wgs = -1;
+};
+
 bool log_enabled();
 // Compute units of the current device (0 if the runtime cannot say); the
 // persistent launches size their grids by it.  Host only.

@@ -227,3 +227,23 @@ def test_binding_rejects_mismatched_operands(S):
         S.sdpa_fwd(q, k, k, bias=torch.zeros(1, 2, 16, 16, dtype=torch.float32))
     with pytest.raises(TypeError, match="dout must be"):
         S.sdpa_bwd(q, k, k, q, q.float(), torch.zeros(1, 2, 16))
+
+
+def test_launch_config_overrides_are_validated(S, monkeypatch):
+    """SDPA_FWD_CONFIG / SDPA_BWD_CONFIG (the run-time launch configuration,
+    as oneDNN's SDPA_CONFIG / BWD_SDPA_CONFIG for its tile choices): a
+    malformed value is an argument error of every call, reported before
+    anything is launched (so the fake pointers here are never used)."""
+    L = S.lib()
+    bad = [("SDPA_FWD_CONFIG", "heads=0", b"head groups"), ("SDPA_FWD_CONFIG", "heads=65", b"head groups"),
+           ("SDPA_FWD_CONFIG", "wgs=12", b"multiples of 8"), ("SDPA_FWD_CONFIG", "tile=3", b"unknown key"),
+           ("SDPA_FWD_CONFIG", "heads", b"key=value"), ("SDPA_FWD_CONFIG", "heads=x", b"bad value"),
+           ("SDPA_FWD_CONFIG", "heads=4,wgs=-5", b"bad value"), ("SDPA_BWD_CONFIG", "dkdv_wgs=100", b"multiples of 8"),
+           ("SDPA_BWD_CONFIG", "dq_heads=2,dkdv_heads=70", b"head groups"), ("SDPA_BWD_CONFIG", "heads=2", b"unknown key")]
+    for name, val, msg in bad:
+        monkeypatch.setenv(name, val)
+        assert _fwd(S, _problem(S)) == S.SDPA_ERR_INVALID_ARG, (name, val)
+        assert msg in L.sdpa_last_error_message(), (name, val, L.sdpa_last_error_message())
+        assert _bwd(S, _problem(S)) == S.SDPA_ERR_INVALID_ARG, (name, val)
+        assert msg in L.sdpa_last_error_message(), (name, val, L.sdpa_last_error_message())
+        monkeypatch.delenv(name)

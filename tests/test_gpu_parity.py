@@ -643,6 +643,41 @@ def test_backward_is_deterministic(S):
             assert torch.equal(a_, b_)
 
 
+@pytest.mark.parametrize("case", ["d128_causal", "d64_gqa"])
+def test_launch_config_does_not_change_results(S, monkeypatch, case):
+    # The run-time launch configuration (SDPA_FWD_CONFIG / SDPA_BWD_CONFIG:
+    # head groups of the XCD placement, workgroup counts of the streamed
+    # forward and dK/dV) moves work between workgroups but not the order of
+    # any sum, so every output is bitwise the same: down to 8 workgroups
+    # (16+ units each), one unit per workgroup, and odd head groups.
+    if case == "d128_causal":
+        wl = inputs.small("bf16", b=2, h=8, s_q=1000, s_kv=1000, causal=True, seed=71)
+    else:
+        wl = inputs.small("f16", b=3, h=6, s_q=333, s_kv=517, d_qk=64, d_v=64, h_kv=2, seed=72)
+    x = inputs.make_inputs(wl)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "dout"))
+    kw = dict(causal=wl.causal)
+
+    def run():
+        o, lse, _ = S.sdpa_fwd(q, k, v, **kw)
+        dq, dk, dv, _ = S.sdpa_bwd(q, k, v, o, do, lse, **kw)
+        torch.cuda.synchronize()
+        return o, lse, dq, dk, dv
+
+    want = run()
+    for fwd_cfg, bwd_cfg in (("heads=1,wgs=16", "dq_heads=8,dkdv_heads=1,dkdv_wgs=8"),
+                             ("wgs=0", "dkdv_wgs=0"),
+                             ("heads=3,wgs=24", "dq_heads=5,dkdv_heads=3,dkdv_wgs=40")):
+        monkeypatch.setenv("SDPA_FWD_CONFIG", fwd_cfg)
+        monkeypatch.setenv("SDPA_BWD_CONFIG", bwd_cfg)
+        _say(case, fwd_cfg, bwd_cfg)
+        got = run()
+        for name, a_, b_ in zip(("o", "lse", "dq", "dk", "dv"), want, got):
+            assert torch.equal(a_, b_), (case, fwd_cfg, bwd_cfg, name)
+    monkeypatch.delenv("SDPA_FWD_CONFIG")
+    monkeypatch.delenv("SDPA_BWD_CONFIG")
+
+
 def test_preprocess_matches_oracle_D(S):
     wl = inputs.small("bf16", b=2, h=3, s_q=333, s_kv=333, causal=True, seed=21)
     x = inputs.make_inputs(wl)
