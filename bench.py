@@ -106,17 +106,22 @@ def cpu_baseline(wl, x, budget_heads):
 
 class CacheFlush:
     """Writes a 512 MiB device buffer, so that neither the 256 MB Infinity
-    Cache nor the L2s hold any input of the next call.  Called before each
-    timed iteration of the memory-bound measurements, outside the interval
-    the events bracket."""
+    Cache nor the L2s hold any input of the next call, then reads a second
+    512 MiB buffer, so that the lines the write left dirty are written back
+    to HBM before the call instead of during it (the caches then hold clean
+    lines of the read buffer, which the call's own reads evict for free).
+    Called before each timed iteration of the memory-bound measurements,
+    outside the interval the events bracket."""
 
     def __init__(self, torch, dev, mib=512):
         self.buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+        self.clean = torch.ones((mib << 20) // 4, dtype=torch.int32, device=dev)
         self.n = 0
 
     def __call__(self):
         self.n += 1
         self.buf.fill_(self.n & 0xFF)
+        self.clean.sum()
 
 
 def _median(xs):
