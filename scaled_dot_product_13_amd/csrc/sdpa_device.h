@@ -311,9 +311,14 @@ template <int D, typename T> struct RowReader {
   }
 };
 
-template <int D, typename T> struct TrReader {
+// HOIST: keep the swizzled offsets of every 32-column block in registers
+// (2 D / 32 of them) instead of forming each with a v_xor at its read, for
+// kernels with registers to spare and vector work to save.
+template <int D, typename T, bool HOIST = false> struct TrReader {
   static constexpr bool FAST = (D == 64 || D == 128);
+  static constexpr int NX = HOIST ? D / 32 : 1;
   uint32_t pre[2];  // byte offsets of the two 4-row halves at kb = mb = 0
+  uint32_t px[NX][2];  // (HOIST) pre[h] ^ 64 m: the halves' offsets at MB = 32 m
   int lane_;
   __device__ __forceinline__ void init(int lane) {
     lane_ = lane;
@@ -323,6 +328,8 @@ template <int D, typename T> struct TrReader {
       const int row = 8 * (G >> 1) + 4 * h + (i >> 2);
       const int col = 16 * (G & 1) + 4 * (i & 3);
       pre[h] = (uint32_t)(2 * Lds<D>::off(row, col));
+#pragma unroll
+      for (int m = 0; m < NX; ++m) px[m][h] = pre[h] ^ (uint32_t)(64 * m);
     }
   }
   struct View {
@@ -352,7 +359,8 @@ template <int D, typename T> struct TrReader {
     if constexpr (FAST) {
       const char* base = (const char*)tile + kb * D * 2;
       constexpr uint32_t x = (uint32_t)(64 * (MB / 32));
-      const uint32_t o0 = xor_at_use<x>(pre[0]), o1 = xor_at_use<x>(pre[1]);
+      const uint32_t o0 = HOIST ? px[MB / 32][0] : xor_at_use<x>(pre[0]);
+      const uint32_t o1 = HOIST ? px[MB / 32][1] : xor_at_use<x>(pre[1]);
       s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o0));
       s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o1));
       u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);

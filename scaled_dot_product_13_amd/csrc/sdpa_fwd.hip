@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
   float m_run = -1e30f, l_run = 0.f;  // m_run in scaled log2 units
 
   RowReader<DQK, T> rdK;
-  TrReader<DV, T> rdV;
+  TrReader<DV, T, true> rdV;
   rdK.init(lane);
   rdV.init(lane);
 
