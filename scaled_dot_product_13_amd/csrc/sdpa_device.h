@@ -299,6 +299,19 @@ template <int D, typename T> struct RowReader {
   __device__ __forceinline__ View view(const T* tile) const {
     return View{lds_addr(tile) + pre, tile, lane_};
   }
+  // read<T_>(tile, 32 b) for b = 0 .. NB-1, sharing the swizzled offset
+  template <int T_, int NB>
+  __device__ __forceinline__ void read_blocks(const T* tile, u32x4 (&out)[NB]) const {
+    if constexpr (FAST) {
+      const uint32_t off = xor_at_use<32u * T_>(pre);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        out[b] = *reinterpret_cast<const u32x4*>((const char*)tile + off + (uint32_t)(32 * b * D * 2));
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) out[b] = lds_rowA<D>(tile, 32 * b, 16 * T_, lane_);
+    }
+  }
   // X[mb + sig(l32)][16 t + 8g + e]; mb a multiple of 32
   template <int T_>
   __device__ __forceinline__ u32x4 read(const T* tile, int mb) const {

@@ -134,7 +134,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
   float m_run = -1e30f, l_run = 0.f;  // m_run in scaled log2 units
 
   RowReader<DQK, T> rdK;
-  TrReader<DV, T, true> rdV;
+  // (registers to spare only at d <= 128 without bias or dropout)
+  TrReader<DV, T, !BIAS && !DROP && DQK + DV <= 256> rdV;
   rdK.init(lane);
   rdV.init(lane);
 
@@ -185,8 +186,10 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     u32x4 kop[LEAN ? 1 : NBLK * KT];
     if (!LEAN && active) {
       static_for<KT>([&](auto t) __attribute__((always_inline)) {
+        u32x4 kb2[NBLK];
+        rdK.template read_blocks<t>(cK, kb2);
 #pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = rdK.template read<t>(cK, 32 * blk);
+        for (int blk = 0; blk < NBLK; ++blk) kop[NBLK * t + blk] = kb2[blk];
       });
     }
 
