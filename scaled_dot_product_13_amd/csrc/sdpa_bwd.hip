@@ -767,7 +767,8 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
   }
   RowReader<DQK, T> rdK;
   RowReader<DV, T> rdV;
-  TrReader<DQK, T> rdKt;
+  // (the transposed reads' offsets held in registers where they fit)
+  TrReader<DQK, T, !BIAS && !DROP && DQK + DV <= 256> rdKt;
   rdK.init(lane);
   rdV.init(lane);
   rdKt.init(lane);
@@ -793,7 +794,14 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
     // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
     static_for<KT>([&](auto t) __attribute__((always_inline)) {
-      const u32x4 a0 = rdK.template read<t>(cK, 0), a1 = rdK.template read<t>(cK, 32);
+      u32x4 ab[2];
+      if constexpr (BIAS) {
+        ab[0] = rdK.template read<t>(cK, 0);
+        ab[1] = rdK.template read<t>(cK, 32);
+      } else {
+        rdK.template read_blocks<t>(cK, ab);  // one swizzled offset for both blocks
+      }
+      const u32x4 a0 = ab[0], a1 = ab[1];
       s[0] = mfma32<T>(a0, qreg[t], s[0]);
       s[1] = mfma32<T>(a1, qreg[t], s[1]);
     });
@@ -820,7 +828,14 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
       }
     }
     static_for<VT>([&](auto t) __attribute__((always_inline)) {
-      const u32x4 a0 = rdV.template read<t>(cV, 0), a1 = rdV.template read<t>(cV, 32);
+      u32x4 ab[2];
+      if constexpr (BIAS) {
+        ab[0] = rdV.template read<t>(cV, 0);
+        ab[1] = rdV.template read<t>(cV, 32);
+      } else {
+        rdV.template read_blocks<t>(cV, ab);  // one swizzled offset for both blocks
+      }
+      const u32x4 a0 = ab[0], a1 = ab[1];
       dp[0] = mfma32<T>(a0, doreg[t], dp[0]);
       dp[1] = mfma32<T>(a1, doreg[t], dp[1]);
     });
