@@ -353,12 +353,10 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     }
     if (block_needs_mask(q0)) {
       keep_branch();
+      // row q0 + 8 g + 16 (r >> 3) + (r & 7) against this lane's key
+      const TileWindow win = kv_ok ? rows_of_key(kvr, bd, BAND, sq, q0 + 8 * g) : tile_window(1, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = q0 + 16 * (r >> 3) + 8 * g + (r & 7);
-        const bool vis = qr < sq && kv_ok && (!BAND || (kvr - qr >= bd.lo && kvr - qr <= bd.hi));
-        pv[r] = vis ? pv[r] : 0.f;
-      }
+      for (int r = 0; r < 16; ++r) pv[r] = win.has(16 * (r >> 3) + (r & 7)) ? pv[r] : 0.f;
     }
     // hand P to role B in the io type (P >= 0, so under dropout the sign bit
     // of each element marks it dropped); pb is P o Z for the dV product
@@ -882,14 +880,11 @@ __global__ void __launch_bounds__(256, (DqOcc<DQK, DV, DROP, BAND, BIAS>::value)
         (n0 + BC > skv) || (BAND && !(n0 - (wq0 + 31) >= bd.lo && n0 + BC - 1 - wq0 <= bd.hi));
     if (need_mask) {
       keep_branch();
+      const TileWindow win = keys_of_row(row, bd, BAND, skv, n0 + 8 * g);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-          const bool vis = kv < skv && (!BAND || (kv - row >= bd.lo && kv - row <= bd.hi));
-          s[blk][r] = vis ? s[blk][r] : 0.f;
-        }
+        for (int r = 0; r < 16; ++r) s[blk][r] = win.has(32 * blk + 16 * (r >> 3) + (r & 7)) ? s[blk][r] : 0.f;
     }
     // dS^T = P^T o (dP^T o Z - D), packed as the B operand of dQ^T += K^T dS^T
     u32x4 dsb[4];

@@ -241,9 +241,9 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
     // masked unless every (row, key) of the wave's tile lies inside the band
     const bool need_mask =
         (n0 + BC > skv) || (BAND && !(n0 - (wq0 + 31) >= bd.lo && n0 + BC - 1 - wq0 <= bd.hi));
-    auto visible = [&](int blk, int r) {
-      int kv = n0 + 32 * blk + 16 * (r >> 3) + 8 * g + (r & 7);
-      return kv < skv && (!BAND || (kv - row >= bd.lo && kv - row <= bd.hi));
+    // key n0 + 8 g + o of this lane's row (o = 32 blk + 16 (r >> 3) + (r & 7))
+    auto visible = [&](const TileWindow& win, int blk, int r) {
+      return win.has(32 * blk + 16 * (r >> 3) + (r & 7));
     };
     float mrow;
     if (BIAS) {
@@ -268,10 +268,11 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
       }
       if (need_mask) {
         keep_branch();
+        const TileWindow win = keys_of_row(row, bd, BAND, skv, n0 + 8 * g);
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? s[blk][r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) s[blk][r] = visible(win, blk, r) ? s[blk][r] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -283,10 +284,11 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
       const float hide = pos ? -INFINITY : INFINITY;
       if (need_mask || zs) {
         keep_branch();
+        const TileWindow win = keys_of_row(row, bd, BAND, skv, n0 + 8 * g);
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[blk][r] = visible(blk, r) ? (zs ? 0.f : s[blk][r]) : hide;
+          for (int r = 0; r < 16; ++r) s[blk][r] = visible(win, blk, r) ? (zs ? 0.f : s[blk][r]) : hide;
       }
       float mx = -INFINITY, mn = INFINITY;
       if (pos) {

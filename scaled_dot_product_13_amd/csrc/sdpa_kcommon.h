@@ -125,6 +125,50 @@ __device__ __forceinline__ Band seq_band(int32_t br, int32_t lo, int32_t hi, int
   return b;
 }
 
+// A lane's visible range within a tile, for masks applied to elements at
+// compile-time offsets o (0 <= o < 2^20) from a per-lane base index: the
+// element at base + o is visible iff first <= base + o <= last (absolute,
+// inclusive), tested as one unsigned compare instead of a chain of
+// short-circuit branches.  An empty range never matches.
+struct TileWindow {
+  int32_t first;  // first visible offset, clamped to [0, 2^20]
+  uint32_t span;  // last - first, last clamped to 2^20
+  __device__ __forceinline__ bool has(int o) const { return (uint32_t)(o - first) <= span; }
+};
+__device__ __forceinline__ TileWindow tile_window(int64_t first_abs, int64_t last_abs, int64_t base) {
+  constexpr int64_t kOffMax = 1 << 20;
+  int64_t f = first_abs - base, l = last_abs - base;
+  f = f < 0 ? 0 : f;
+  l = l > kOffMax ? kOffMax : l;
+  TileWindow w;
+  if (l < f) {  // empty (or wholly outside [0, 2^20])
+    w.first = (int32_t)(2 * kOffMax);
+    w.span = 0;
+  } else {
+    w.first = (int32_t)f;
+    w.span = (uint32_t)(l - f);
+  }
+  return w;
+}
+// Keys visible from row `row` (band mask and sequence end): [first, last].
+// (The row is made opaque so that the window is formed where it is used,
+// not hoisted out of the tile loop into registers held across it.)
+__device__ __forceinline__ TileWindow keys_of_row(int row, const Band& bd, bool band, int skv,
+                                                  int64_t base) {
+  __asm__ volatile("" : "+v"(row));
+  const int64_t first = band ? (int64_t)row + bd.lo : 0;
+  const int64_t last = band ? min((int64_t)skv - 1, (int64_t)row + bd.hi) : (int64_t)skv - 1;
+  return tile_window(first, last, base);
+}
+// Rows that see key `kv` (band mask and sequence end): [kv - hi, kv - lo].
+__device__ __forceinline__ TileWindow rows_of_key(int kv, const Band& bd, bool band, int sq,
+                                                  int64_t base) {
+  __asm__ volatile("" : "+v"(kv));
+  const int64_t first = band ? (int64_t)kv - bd.hi : 0;
+  const int64_t last = band ? min((int64_t)sq - 1, (int64_t)kv - bd.lo) : (int64_t)sq - 1;
+  return tile_window(first, last, base);
+}
+
 // ALiBi of one (sequence, head): the term is slope * |j - i - off|
 // (slope already negated), zero slope when there is none.
 struct AlibiTerm {
