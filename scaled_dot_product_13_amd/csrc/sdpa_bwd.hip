@@ -30,6 +30,15 @@
 #define SDPA_DKDV_BIAS_LDS_MAXD 192
 #endif
 
+// Role A of a dK/dV trip of two query blocks: 0 runs the blocks one after
+// the other; 1 interleaves one block's exponentials with the other's matrix
+// products in source order; 2 (default) also pins that order with empty
+// scheduling barriers (the compiler otherwise groups the products together).
+#ifndef SDPA_DKDV_PIPE
+#define SDPA_DKDV_PIPE 2
+#endif
+
+
 namespace sdpa {
 
 // ---------------------------------------------------------------------------
@@ -279,15 +288,13 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     auto block_active = [&](int q0) __attribute__((always_inline)) {
       return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
     };
+    // (bitwise, so that evaluating it needs no branches)
     auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
-      return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
-             (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
+      return (q0 + 32 > sq) | (wk0 + 31 >= skv) |
+             (BAND & !((wk0 - (q0 + 31) >= bd.lo) & (wk0 + 31 - q0 <= bd.hi)));
     };
     const bool bias_lds = bias_lds_of(u);
-   static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
-    constexpr int QB2 = decltype(qbc)::value;  // query block within the trip
-    const int q0 = it.q0 + 32 * QB2, h = it.h;
-    if (QBLK > 1 && !block_active(q0)) return;
+    const int h = it.h;
     const uint32_t bh = (uint32_t)(b * a.H + h);
     const uint16_t* bg = BIAS ? bias_head(b, h) : nullptr;
     const AlibiTerm at = alibi_term(a.alibi, a.alibi_sb, a.alibi_br, b, h, sq, skv);
@@ -298,70 +305,105 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     // the dV operands before the element-wise work.
     // (in two halves when there are more than 8 operands, to bound registers)
     constexpr int KH = KT > 8 ? KT / 2 : KT;
-    u32x4 qop[KH];
-    f32x16 s = f32x16{};
-    static_for<KT / KH>([&](auto hf) __attribute__((always_inline)) {
-      static_for<KH>([&](auto j) __attribute__((always_inline)) {
-        qop[j] = vQ.template read<hf * KH + j>(32 * QB2);
-      });
-#pragma unroll
-      for (int j = 0; j < KH; ++j) s = mfma32<T>(qop[j], reg[hf * KH + j], s);
-    });
     // dV operands: requested before the element-wise work, unless the
     // element-wise work itself needs the registers (bias, wide Q/K rows)
     constexpr bool EARLY_O = !BIAS && DQK <= 128;
-    u32x4 oop[2 * VB];
-    auto read_oop = [&]() __attribute__((always_inline)) {
+    // S = Q K^T of query block QB2
+    // (hook(n) runs after the n-th product)
+    auto scores = [&](auto qbc, auto&& hook) __attribute__((always_inline)) {
+      constexpr int QB2 = decltype(qbc)::value;
+      u32x4 qop[KH];
+      f32x16 s = f32x16{};
+      static_for<KT / KH>([&](auto hf) __attribute__((always_inline)) {
+        static_for<KH>([&](auto j) __attribute__((always_inline)) {
+          qop[j] = vQ.template read<hf * KH + j>(32 * QB2);
+        });
+        static_for<KH>([&](auto j) __attribute__((always_inline)) {
+          s = mfma32<T>(qop[j], reg[hf * KH + j], s);
+          hook(std::integral_constant<int, hf * KH + j>{});
+        });
+      });
+      return s;
+    };
+    auto read_oop = [&](auto qbc, u32x4 (&oop)[2 * VB]) __attribute__((always_inline)) {
+      constexpr int QB2 = decltype(qbc)::value;
       static_for<VB>([&](auto vb) __attribute__((always_inline)) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) oop[tt * VB + vb] = vOt.template read<32 * vb>(16 * tt + 32 * QB2);
       });
     };
-    if constexpr (EARLY_O) read_oop();
-    uint32_t kw[8];
-    if (DROP) {
-      // 4x4 patches along this lane's queries (the first 4 of the 8 used)
-      uint32_t var4[8];
+    // P = exp2(c S + log2e bias - LSE log2e) of block QB2 (unmasked)
+    auto exps = [&](auto qbc, const f32x16& s, float (&pv)[16]) __attribute__((always_inline)) {
+      constexpr int QB2 = decltype(qbc)::value;
+      const int q0 = it.q0 + 32 * QB2;
+      const float* cL = sL[set] + 32 * QB2;
+      const T* cB = sB[BIAS_LDS ? set : 0];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
-      quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
-    }
-    const float* cL = sL[set] + 32 * QB2;
-    const T* cB = sB[BIAS_LDS ? set : 0];
-    float pv[16];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int lb = 16 * hh + 8 * g;  // first of my 8 consecutive rows
+        const f32x4 L0 = *(const f32x4*)(cL + lb), L1 = *(const f32x4*)(cL + lb + 4);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int lb = 16 * hh + 8 * g;  // first of my 8 consecutive rows
-      const f32x4 L0 = *(const f32x4*)(cL + lb), L1 = *(const f32x4*)(cL + lb + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * hh + e;
-        float x = -(e < 4 ? L0[e] : L1[e - 4]);  // exponent = c s + log2e bias - LSE log2e
-        if (BIAS) {
-          const int ql = 32 * QB2 + lb + e, qr = q0 + lb + e;
-          float bval = 0.f;
-          if (alibi)
-            bval = alibi_at(at, kvr, qr);
-          else if (bias_lds)
-            bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * kb + l32)));
-          else if (kv_ok && qr < sq)
-            bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
-          x = __builtin_fmaf(bval, kLog2e, x);
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hh + e;
+          float x = -(e < 4 ? L0[e] : L1[e - 4]);  // exponent = c s + log2e bias - LSE log2e
+          if (BIAS) {
+            const int ql = 32 * QB2 + lb + e, qr = q0 + lb + e;
+            float bval = 0.f;
+            if (alibi)
+              bval = alibi_at(at, kvr, qr);
+            else if (bias_lds)
+              bval = to_f32<T>(*(const uint16_t*)(cB + Lds<BC>::off(ql, 32 * kb + l32)));
+            else if (kv_ok && qr < sq)
+              bval = to_f32<T>(bg[(int64_t)qr * a.sb_.s + kvr]);
+            x = __builtin_fmaf(bval, kLog2e, x);
+          }
+          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, x));
         }
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, x));
       }
-    }
-    if (block_needs_mask(q0)) {
-      keep_branch();
-      // row q0 + 8 g + 16 (r >> 3) + (r & 7) against this lane's key
-      const TileWindow win = kv_ok ? rows_of_key(kvr, bd, BAND, sq, q0 + 8 * g) : tile_window(1, 0, 0);
+    };
+    // without bias: the exponent's offsets -LSE log2e of block QB2's rows,
+    // and element r's probability
+    auto neg_lse = [&](auto qbc, float (&nl)[16]) __attribute__((always_inline)) {
+      constexpr int QB2 = decltype(qbc)::value;
+      const float* cL = sL[set] + 32 * QB2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pv[r] = win.has(16 * (r >> 3) + (r & 7)) ? pv[r] : 0.f;
-    }
-    // hand P to role B in the io type (P >= 0, so under dropout the sign bit
-    // of each element marks it dropped); pb is P o Z for the dV product
-    u32x4 pb[2];
-    {
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 L0 = *(const f32x4*)(cL + 16 * hh + 8 * g), L1 = *(const f32x4*)(cL + 16 * hh + 8 * g + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nl[8 * hh + e] = -L0[e];
+          nl[8 * hh + 4 + e] = -L1[e];
+        }
+      }
+    };
+    auto exp_at = [&](const f32x16& s, const float (&nl)[16], int r) __attribute__((always_inline)) {
+      return __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nl[r]));
+    };
+    // masks P of block QB2, hands it to role B and returns P o Z packed as
+    // the dV product's B operand
+    // (dropout) the keep bytes of block QB2: 4x4 patches along this lane's
+    // queries (the first 4 of the 8 used)
+    auto keep_words = [&](auto qbc, uint32_t (&kw)[8]) __attribute__((always_inline)) {
+      if (DROP) {
+        const int q0 = it.q0 + 32 * decltype(qbc)::value;
+        uint32_t var4[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) var4[k] = (uint32_t)((q0 + 16 * (k >> 1) + 8 * g) >> 2) + (k & 1);
+        quad_keep_words<false>(var4, (uint32_t)kvr >> 2, bh, dk.off, dk.k0, dk.k1, lane, kw);
+      }
+    };
+    auto finish = [&](auto qbc, float (&pv)[16], const uint32_t (&kw)[8], u32x4 (&pb)[2]) __attribute__((always_inline)) {
+      constexpr int QB2 = decltype(qbc)::value;
+      const int q0 = it.q0 + 32 * QB2;
+      if (block_needs_mask(q0)) {
+        keep_branch();
+        // row q0 + 8 g + 16 (r >> 3) + (r & 7) against this lane's key
+        const TileWindow win = kv_ok ? rows_of_key(kvr, bd, BAND, sq, q0 + 8 * g) : tile_window(1, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = win.has(16 * (r >> 3) + (r & 7)) ? pv[r] : 0.f;
+      }
+      // hand P to role B in the io type (P >= 0, so under dropout the sign
+      // bit of each element marks it dropped)
       u32x4 ph[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -386,14 +428,77 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
       const uint32_t pa = p_lane + (uint32_t)(i & 1) * P_SLOT + 2048 * QB2;
 #pragma unroll
       for (int j = 0; j < 2; ++j) *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(pa + 1024 * j) = ph[j];
-    }
+    };
     // dV^T += dO^T (P o Z)
-    if constexpr (!EARLY_O) read_oop();
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) acc[vb] = mfma32<T>(oop[tt * VB + vb], pb[tt], acc[vb]);
-   });
+    auto dv = [&](const u32x4 (&oop)[2 * VB], const u32x4 (&pb)[2], auto&& hook) __attribute__((always_inline)) {
+      static_for<2 * VB>([&](auto n) __attribute__((always_inline)) {
+        constexpr int tt = n / VB, vb = n % VB;
+        acc[vb] = mfma32<T>(oop[tt * VB + vb], pb[tt], acc[vb]);
+        hook(n);
+      });
+    };
+    auto none = [](auto) {};
+    // one block, phase after phase
+    auto block = [&](auto qbc) __attribute__((always_inline)) {
+      const f32x16 s = scores(qbc, none);
+      u32x4 oop[2 * VB], pb[2];
+      if constexpr (EARLY_O) read_oop(qbc, oop);
+      uint32_t kw[8];
+      keep_words(qbc, kw);
+      float pv[16];
+      exps(qbc, s, pv);
+      finish(qbc, pv, kw, pb);
+      if constexpr (!EARLY_O) read_oop(qbc, oop);
+      dv(oop, pb, none);
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, QBLK - 1>;
+    if constexpr (QBLK == 1) {
+      block(B0{});
+    } else {
+      static_assert(QBLK == 2 && !BIAS && !DROP, "two-block trips are for plain attention");
+      if (SDPA_DKDV_PIPE) {
+        // The first block's exponentials are interleaved with the second
+        // block's score products, and the second block's exponentials with
+        // the first block's dV products, so that one wave's matrix products
+        // and vector work overlap (the empty scheduling barriers keep the
+        // compiler from regrouping them).  A block none of the wave's keys
+        // see (at most one of the two, on the band's edge) goes through the
+        // same steps: its mask leaves P = 0, which adds nothing to dV, and
+        // role B skips it.
+        auto fence = []() __attribute__((always_inline)) {
+          if (SDPA_DKDV_PIPE >= 2) __builtin_amdgcn_sched_barrier(0);
+        };
+        const f32x16 s0 = scores(B0{}, none);
+        float nl[16], pv0[16], pv1[16];
+        neg_lse(B0{}, nl);
+        u32x4 oop0[2 * VB], oop1[2 * VB], pb[2];
+        read_oop(B0{}, oop0);
+        // the elements r with r N / 16 = n after the n-th of N products
+        auto share = [&](auto n, auto nn, const f32x16& sc, float (&pv)[16]) __attribute__((always_inline)) {
+          fence();
+          static_for<16>([&](auto r) __attribute__((always_inline)) {
+            if constexpr (decltype(r)::value * decltype(nn)::value / 16 == decltype(n)::value) pv[r] = exp_at(sc, nl, r);
+          });
+          fence();
+        };
+        const f32x16 s1 = scores(B1{}, [&](auto n) __attribute__((always_inline)) {
+          share(n, std::integral_constant<int, KT>{}, s0, pv0);
+        });
+        const uint32_t kw[8] = {};  // (no dropout here)
+        finish(B0{}, pv0, kw, pb);
+        neg_lse(B1{}, nl);
+        read_oop(B1{}, oop1);
+        dv(oop0, pb, [&](auto n) __attribute__((always_inline)) {
+          share(n, std::integral_constant<int, 2 * VB>{}, s1, pv1);
+        });
+        finish(B1{}, pv1, kw, pb);
+        dv(oop1, pb, none);
+      } else {
+        if (block_active(it.q0)) block(B0{});
+        if (block_active(it.q0 + 32)) block(B1{});
+      }
+    }
   };
 
   // ---- role B: dP, dS, dBias, dK for tile i ---------------------------------
@@ -407,9 +512,10 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     auto block_active = [&](int q0) __attribute__((always_inline)) {
       return !BAND || (wk0 + 31 - q0 >= bd.lo && wk0 - (q0 + 31) <= bd.hi);
     };
+    // (bitwise, so that evaluating it needs no branches)
     auto block_needs_mask = [&](int q0) __attribute__((always_inline)) {
-      return (q0 + 32 > sq) || (wk0 + 31 >= skv) ||
-             (BAND && !(wk0 - (q0 + 31) >= bd.lo && wk0 + 31 - q0 <= bd.hi));
+      return (q0 + 32 > sq) | (wk0 + 31 >= skv) |
+             (BAND & !((wk0 - (q0 + 31) >= bd.lo) & (wk0 + 31 - q0 <= bd.hi)));
     };
    static_for<QBLK>([&](auto qbc) __attribute__((always_inline)) {
     constexpr int QB2 = decltype(qbc)::value;
