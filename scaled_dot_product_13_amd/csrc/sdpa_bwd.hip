@@ -39,6 +39,11 @@
 #endif
 
 
+// dK/dV trips of two query blocks under dropout too
+#ifndef SDPA_DKDV_DROP2
+#define SDPA_DKDV_DROP2 1
+#endif
+
 namespace sdpa {
 
 // ---------------------------------------------------------------------------
@@ -105,7 +110,7 @@ template <typename T, int DQK, int DV, bool BAND, bool BIAS, bool DROP>
 __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
   // QBLK 32-row query blocks per trip (two where the LDS holds them), so
   // that each barrier and P hand-over covers QBLK blocks' products
-  constexpr int QBLK = (!BIAS && !DROP && DQK <= 128 && DV <= 128) ? 2 : 1;
+  constexpr int QBLK = (!BIAS && (!DROP || SDPA_DKDV_DROP2) && DQK <= 128 && DV <= 128) ? 2 : 1;
   constexpr int BC = 128, BQ = 32 * QBLK, NSET = 3;
   // STREAM: a workgroup may take several units (the launch caps the grid at
   // the compute units), and role A's waves load every query-side tile.  The
@@ -456,7 +461,7 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     if constexpr (QBLK == 1) {
       block(B0{});
     } else {
-      static_assert(QBLK == 2 && !BIAS && !DROP, "two-block trips are for plain attention");
+      static_assert(QBLK == 2 && !BIAS, "two-block trips are for attention without bias");
       if (SDPA_DKDV_PIPE) {
         // The first block's exponentials are interleaved with the second
         // block's score products, and the second block's exponentials with
@@ -469,7 +474,13 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         auto fence = []() __attribute__((always_inline)) {
           if (SDPA_DKDV_PIPE >= 2) __builtin_amdgcn_sched_barrier(0);
         };
-        const f32x16 s0 = scores(B0{}, none);
+        // (dropout) the keep bytes of each block, formed among the products
+        // before its mask: the first block's among its own score products,
+        // the second block's among the first block's dV products
+        uint32_t kw0[8], kw1[8];
+        const f32x16 s0 = scores(B0{}, [&](auto n) __attribute__((always_inline)) {
+          if constexpr (DROP && decltype(n)::value == 0) keep_words(B0{}, kw0);
+        });
         float nl[16], pv0[16], pv1[16];
         neg_lse(B0{}, nl);
         u32x4 oop0[2 * VB], oop1[2 * VB], pb[2];
@@ -485,14 +496,14 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         const f32x16 s1 = scores(B1{}, [&](auto n) __attribute__((always_inline)) {
           share(n, std::integral_constant<int, KT>{}, s0, pv0);
         });
-        const uint32_t kw[8] = {};  // (no dropout here)
-        finish(B0{}, pv0, kw, pb);
+        finish(B0{}, pv0, kw0, pb);
         neg_lse(B1{}, nl);
         read_oop(B1{}, oop1);
         dv(oop0, pb, [&](auto n) __attribute__((always_inline)) {
+          if constexpr (DROP && decltype(n)::value == 0) keep_words(B1{}, kw1);
           share(n, std::integral_constant<int, 2 * VB>{}, s1, pv1);
         });
-        finish(B1{}, pv1, kw, pb);
+        finish(B1{}, pv1, kw1, pb);
         dv(oop1, pb, none);
       } else {
         if (block_active(it.q0)) block(B0{});
