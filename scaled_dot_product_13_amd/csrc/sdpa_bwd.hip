@@ -44,6 +44,12 @@
 #define SDPA_DKDV_DROP2 1
 #endif
 
+// a streaming dK/dV wave does not wait for its stationary operands at the
+// first barrier of a unit
+#ifndef SDPA_DKDV_ENTER_NOWAIT
+#define SDPA_DKDV_ENTER_NOWAIT 1
+#endif
+
 namespace sdpa {
 
 // ---------------------------------------------------------------------------
@@ -620,11 +626,15 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
     auto enter = [&](const Unit& u, const SeqPos& sp) __attribute__((always_inline)) {
       const int kvr = u.kv0 + 32 * kb + l32;
       const bool kv_ok = kvr < u.skv;
-      const T* src = IS_A ? base_ptr<T>(a.k, a.sk_, sp, u.hk, false) + (int64_t)kvr * a.sk_.s
-                          : base_ptr<T>(a.v, a.sv_, sp, u.hk, false) + (int64_t)kvr * a.sv_.s;
+      // Lanes past the keys load the last key's row: finite values whose
+      // P (role A's mask) is zero and whose dK / dV are not stored.  The
+      // loads are unconditional, so nothing waits for them until the
+      // products use them (see the trip loop's first wait).
+      const int kvc = min(kvr, u.skv - 1);
+      const T* src = IS_A ? base_ptr<T>(a.k, a.sk_, sp, u.hk, false) + (int64_t)kvc * a.sk_.s
+                          : base_ptr<T>(a.v, a.sv_, sp, u.hk, false) + (int64_t)kvc * a.sv_.s;
 #pragma unroll
-      for (int t = 0; t < NR; ++t)
-        reg[t] = kv_ok ? *(const u32x4*)(src + 16 * t + 8 * g) : u32x4{0, 0, 0, 0};
+      for (int t = 0; t < NR; ++t) reg[t] = *(const u32x4*)(src + 16 * t + 8 * g);
 #pragma unroll
       for (int j = 0; j < NA; ++j) acc[j] = f32x16{};
       if (!IS_A && BAND && want_dbias && kv_ok) {
@@ -716,7 +726,13 @@ __global__ void __launch_bounds__(512, 1) dkdv_mfma(const BwdArgs a) {
         enter(u, sp);
         Item it{u.hk * G, u.q_begin};
         for (int j = 0; j < u.n; ++j, ++gi) {
-          wait_all();
+          // On a unit's first trip the last NR vector loads of this wave are
+          // its stationary operands (issued on entering the unit, after
+          // every tile load and store): the barrier need not wait for them.
+          if (SDPA_DKDV_ENTER_NOWAIT && j == 0)
+            wait_vm_lds<NR>();
+          else
+            wait_all();
           __syncthreads();  // item gi landed; P(gi-1) written; set (gi+1)%3 free
           if constexpr (IS_A) {
             if (j + 1 < u.n) {
