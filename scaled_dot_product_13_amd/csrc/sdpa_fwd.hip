@@ -60,8 +60,8 @@ __global__ void __launch_bounds__(256, (FwdOcc<DQK, DV, DROP, BAND, BIAS>::value
   // some row's max grows by more than TAU (log2 units); until then the
   // probabilities are exp2(x - m_run) <= 2^TAU, exact in fp32 and bf16.
   constexpr float TAU = 8.f;
-  // STREAM: the launch may give a workgroup several units (plain batch-mode
-  // problems without bias or dropout, whose grid is capped at two
+  // STREAM: the launch may give a workgroup several units (problems without
+  // bias or dropout, batch or group mode, whose grid is capped at two
   // workgroups per compute unit)
   constexpr bool STREAM = !BIAS && !DROP;
   __shared__ __attribute__((aligned(1024))) T sK[2][BC * DQK];  // double-buffered tiles
@@ -511,11 +511,13 @@ static hipError_t fwd_dispatch_flags(bool causal, bool bias, bool drop, const Fw
                                      hipStream_t st) {
   dim3 grid = xcd_grid((a.seq.s_q + 127) / 128, a.H, a.B), block(256);
   // the plain instances stream units: as many workgroups as run at once
-  // (their occupancy times the compute units, a multiple of 8)
+  // (their occupancy times the compute units, a multiple of 8), in batch and
+  // group mode alike (group mode: 0.70 -> 0.66 ms on 16 sequences of
+  // U[64, 4096] tokens)
   const int cus = device_cus() / 8 * 8;
 #define SDPA_FWD_CASE(C, BI, DR)                                                 \
   if (causal == C && bias == BI && drop == DR) {                                 \
-    if (!BI && !DR && a.seq.cu_q == nullptr) {                                   \
+    if (!BI && !DR) {                                                            \
       const long cap = a.grid_cap < 0 ? (long)cus * FwdOcc<DQK, DV, DR, C, BI>::value \
                                       : (long)a.grid_cap;                        \
       if (cap > 0 && (long)grid.x > cap) grid.x = (unsigned)cap;                 \
