@@ -330,10 +330,11 @@ sdpa_status_t parse_config_env(const char* name, const char* const* keys, int* c
   return SDPA_OK;
 }
 
-// The launch configuration: defaults, then the environment overrides,
-// validated (head groups 1 .. 64; workgroup counts -1, 0 or a positive
-// multiple of 8).
-sdpa_status_t launch_config(sdpa::LaunchConfig& cfg) {
+// The launch configuration: the defaults (batch or group mode), then the
+// environment overrides, validated (head groups 1 .. 64; workgroup counts
+// -1, 0 or a positive multiple of 8).
+sdpa_status_t launch_config(sdpa::LaunchConfig& cfg, bool group_mode) {
+  cfg = sdpa::LaunchConfig::defaults(group_mode);
   static const char* const fk[] = {"heads", "wgs"};
   int* const fv[] = {&cfg.fwd_heads, &cfg.fwd_wgs};
   if (sdpa_status_t st = parse_config_env("SDPA_FWD_CONFIG", fk, fv, 2); st != SDPA_OK) return st;
@@ -443,7 +444,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
   fill_dropout(p, a.drop);
   {
     sdpa::LaunchConfig cfg;
-    if ((st = launch_config(cfg)) != SDPA_OK) return st;
+    if ((st = launch_config(cfg, a.seq.cu_q != nullptr)) != SDPA_OK) return st;
     a.head_group = cfg.fwd_heads;
     a.grid_cap = cfg.fwd_wgs;
   }
@@ -495,7 +496,7 @@ sdpa_status_t sdpa_fwd(const sdpa_problem_t* p, const void* q, sdpa_strides_t q_
 
 static sdpa_status_t fill_bwd_args(const sdpa_problem_t* p, sdpa::BwdArgs& a) {
   sdpa::LaunchConfig cfg;
-  if (sdpa_status_t st = launch_config(cfg); st != SDPA_OK) return st;
+  if (sdpa_status_t st = launch_config(cfg, p->cu_seqlens_q != nullptr); st != SDPA_OK) return st;
   a.dq_head_group = cfg.dq_heads;
   a.dkdv_head_group = cfg.dkdv_heads;
   a.dkdv_grid_cap = cfg.dkdv_wgs;

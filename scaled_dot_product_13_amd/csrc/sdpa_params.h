@@ -135,10 +135,23 @@ constexpr int64_t kDecodeMaxSq = 16;  // thin-query path: s_q <= 16
 //   SDPA_FWD_CONFIG="heads=4,wgs=512"
 //   SDPA_BWD_CONFIG="dq_heads=4,dkdv_heads=2,dkdv_wgs=256"
 // (any subset of the keys).  Results do not depend on these settings.
+// Packed variable-length batches (group mode) start from their own head
+// groups (measured on 16 sequences of U[64, 4096] tokens, H16 d128, causal:
+// forward 648 -> 569 us with 2, dQ 868 -> 702 us and dK/dV 1333 -> 1016 us
+// with 1).
 struct LaunchConfig {
   int fwd_heads = 4, fwd_wgs = -1;
   int dq_heads = 4;
   int dkdv_heads = 2, dkdv_wgs = -1;
+  static LaunchConfig defaults(bool group_mode) {
+    LaunchConfig c;
+    if (group_mode) {
+      c.fwd_heads = 2;
+      c.dq_heads = 1;
+      c.dkdv_heads = 1;
+    }
+    return c;
+  }
 };
 
 bool log_enabled();
