@@ -72,7 +72,9 @@ def _cmp(name, got, ref, dtype, dD=None):
         assert np.array_equal(np.isneginf(got), empty), "LSE -inf rows differ"
         got, ref = got[~empty], ref[~empty]
     assert np.all(np.isfinite(ref)), name
-    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if ref.size == 0:  # an empty sequence's slice
+        return 0.0
+    err = float(np.max(np.abs(got - ref)))
     if _FLAT is not None and name != "lse" and dtype != torch.float32:
         # elements beyond the literal flat bar (reported, not asserted)
         n_over, n_all = _FLAT.get(name, (0, 0))
@@ -519,6 +521,15 @@ def test_strided_bshd_layout(S):
 def test_small_varlen(S, lengths):
     wl = inputs.small("bf16", h=2, causal=True, varlen=(len(lengths), 1, 300), seed=len(lengths))
     run_workload(S, wl, lengths=lengths)
+
+
+@pytest.mark.parametrize("lengths,kv_lengths,causal", [([0, 200, 0, 64], None, True),
+                                                       ([100, 50, 0], [0, 80, 30], False)])
+def test_varlen_empty_sequences(S, lengths, kv_lengths, causal):
+    """Group mode with empty sequences: no query rows (no work, zero dK/dV for
+    their keys) or no keys (O = 0, LSE = -inf, dQ = 0 for their rows)."""
+    wl = inputs.small("bf16", h=2, causal=causal, varlen=(len(lengths), 1, 300), seed=13)
+    run_workload(S, wl, lengths=lengths, kv_lengths=kv_lengths)
 
 
 def test_varlen_non_causal_f16(S):
